@@ -1,0 +1,7 @@
+"""fp64 CPU oracle of the WSVD low-rank decode step.
+
+Test infrastructure: imported only by the tests, the package smoke check
+and the benchmark's CPU-baseline leg.  Never part of the GPU path.
+"""
+from .wsvd_oracle import *  # noqa: F401,F403
+from .wsvd_oracle import __all__  # noqa: F401

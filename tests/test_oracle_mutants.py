@@ -1,0 +1,187 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check the pins catch each.
+
+Every mutant below is a small, believable slip -- a dropped term, a wrong
+sign, a wrong index, a transposed operand, a truncation instead of a
+rounding.  The test applies it to the oracle module, runs every pin in
+test_oracle_pins.py and requires at least one of them to fail.
+"""
+import inspect
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.wsvd_oracle as W
+
+from . import test_oracle_pins as P
+
+
+def _pins():
+    out = []
+    for name, fn in inspect.getmembers(P, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if not params:
+            out.append((name, fn, {}))
+            continue
+        argnames, values = params[0].args
+        argnames = [a.strip() for a in argnames.split(",")]
+        for v in values:
+            v = v if isinstance(v, tuple) else (v,)
+            out.append((f"{name}{v}", fn, dict(zip(argnames, v))))
+    return out
+
+
+PINS = _pins()
+
+
+def _softmax_nomax(s):
+    e = np.exp(s)
+    return e / np.sum(e)
+
+
+def _softmax_sign(s):
+    m = np.max(s)
+    e = np.exp(m - s)
+    return e / np.sum(e)
+
+
+def _upcast_bad_shift(a, dt, _orig=W.upcast):
+    if dt == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+        return bits.view(np.float32).astype(np.float64)
+    return _orig(a, dt)
+
+
+def _dequant_noscale(C, C_dt, scale=None):
+    return W.upcast(C, C_dt)
+
+
+def _split_floor(ell, S):
+    chunk = ell // S
+    return [(min(ell, s * chunk), min(ell, (s + 1) * chunk)) for s in range(S)]
+
+
+def _combine_badweight(o_parts, lse_parts):
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    o = np.asarray(o_parts, dtype=np.float64)
+    if not np.any(np.isfinite(lse)):
+        return np.zeros(o.shape[-1])
+    M = np.max(lse)
+    w = np.where(np.isfinite(lse), np.exp(M - lse), 0.0)
+    return (w @ o) / np.sum(w)
+
+
+def _combine_nonorm(o_parts, lse_parts):
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    o = np.asarray(o_parts, dtype=np.float64)
+    if not np.any(np.isfinite(lse)):
+        return np.zeros(o.shape[-1])
+    w = np.where(np.isfinite(lse), np.exp(lse - np.max(lse)), 0.0)
+    return w @ o
+
+
+def _segment_nom(q, K, V, sigma, a, e):
+    H = V.shape[1]
+    if e <= a:
+        return np.zeros(H), -math.inf
+    s = sigma * (K[a:e] @ q)
+    m = np.max(s)
+    w = np.exp(s - m)
+    return (w / w.sum()) @ V[a:e], float(math.log(w.sum()))
+
+
+def _attend_k_for_v(q, K, V, sigma):
+    return W.softmax_weights(sigma * (K @ q)) @ K if K.shape == V.shape else W.softmax_weights(sigma * (K @ q)) @ V
+
+
+def _attend_nosigma(q, K, V, sigma):
+    return W.softmax_weights(K @ q) @ V
+
+
+def _attend_sigma_sq(q, K, V, sigma):
+    return W.softmax_weights(sigma * sigma * (K @ q)) @ V
+
+
+def _reconstruct_transposed(c, B):
+    if B.shape[0] == B.shape[1]:
+        return c @ B.T
+    return c @ B
+
+
+def _reconstruct_drop_last_rank(c, B):
+    return c[:, :-1] @ B[:-1] if B.shape[0] > 1 else c @ B
+
+
+def _append_shifted(x, x_dt, A, A_dt, nh, r):
+    xx = W.upcast(x, x_dt); AA = W.upcast(A, A_dt)
+    c = np.zeros((xx.shape[0], nh, r))
+    for h in range(nh):
+        lo = min(h * r + 1, AA.shape[1] - r)
+        c[:, h, :] = xx @ AA[:, lo:lo + r]
+    return c
+
+
+def _round_truncate(v):
+    v = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _round_half_up(v):
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros(v.shape)
+    nz = v != 0
+    m, e = np.frexp(v[nz])
+    qn = np.ldexp(1.0, np.maximum(e - 8, -133))
+    out[nz] = np.floor(v[nz] / qn + 0.5) * qn
+    return (out.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _decode_one_short(inp, b, h, softmax_scale=None, *, C_K=None, C_V=None, _orig=W.decode_attn_one):
+    import copy
+    j = copy.copy(inp)
+    j.L = np.maximum(np.asarray(inp.L) - 1, 1)
+    return _orig(j, b, h, softmax_scale, C_K=C_K, C_V=C_V)
+
+
+MUTANTS = {
+    "softmax without max shift": ("softmax_weights", _softmax_nomax),
+    "softmax sign flipped": ("softmax_weights", _softmax_sign),
+    "bf16 upcast shifted by 15": ("upcast", _upcast_bad_shift),
+    "int8 scale dropped": ("dequant_latent", _dequant_noscale),
+    "split chunk floor instead of ceil": ("split_bounds", _split_floor),
+    "merge weight sign flipped": ("combine", _combine_badweight),
+    "merge not normalised": ("combine", _combine_nonorm),
+    "segment lse drops the max": ("segment_attend", _segment_nom),
+    "K used in place of V": ("attend", _attend_k_for_v),
+    "softmax scale dropped": ("attend", _attend_nosigma),
+    "softmax scale squared": ("attend", _attend_sigma_sq),
+    "factor transposed": ("reconstruct", _reconstruct_transposed),
+    "last rank term dropped": ("reconstruct", _reconstruct_drop_last_rank),
+    "append head block off by one": ("append_latents", _append_shifted),
+    "bf16 rounding truncates": ("round_to_bf16_bits", _round_truncate),
+    "bf16 rounding ties away": ("round_to_bf16_bits", _round_half_up),
+    "one token short": ("decode_attn_one", _decode_one_short),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(W, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pname, pin, kw in PINS:
+        try:
+            pin(**kw)
+        except Exception:  # assertion or numerical failure
+            caught.append(pname)
+    assert caught, f"no pin caught mutant: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pname, pin, kw in PINS:
+        pin(**kw)

@@ -1,0 +1,351 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test ties one part of the oracle to a closed form, a library routine,
+an exact invariant, or hand-checked values, so a dropped term, wrong sign,
+wrong index or transposed operand fails at least one of them (see
+test_oracle_mutants.py, which plants such mistakes and checks that).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+import torch
+
+import oracle as O
+from rank_kv_cache_flash_amd.inputs import DecodeInputs
+
+RNG = np.random.default_rng(12345)
+
+
+def _inp_f64(q, CK, CV, BK, BV, L=None, s_K=None, s_V=None, C_dt="f64"):
+    """Wrap float64 arrays as a one-sequence DecodeInputs ([1, nh, ...])."""
+    q = np.asarray(q)[None] if q.ndim == 2 else np.asarray(q)
+    CK = CK[None] if CK.ndim == 3 else CK
+    CV = CV[None] if CV.ndim == 3 else CV
+    nb, nh, L_cap, r = CK.shape
+    H = q.shape[-1]
+    L = np.full(nb, L_cap, np.int32) if L is None else np.asarray(L, np.int32)
+    return DecodeInputs(nb=nb, nh=nh, H=H, r=r, L_cap=L_cap, q=q, q_dt="f64", C_K=CK, C_V=CV,
+                        C_dt=C_dt, B_K=BK, B_V=BV, B_dt="f64", L=L, out_dt="f64",
+                        s_K=s_K, s_V=s_V)
+
+
+def _sdpa(q, K, V, sigma):
+    """torch's scaled_dot_product_attention in float64 on the CPU."""
+    qt = torch.tensor(q, dtype=torch.float64).reshape(1, 1, 1, -1)
+    Kt = torch.tensor(K, dtype=torch.float64).reshape(1, 1, K.shape[0], -1)
+    Vt = torch.tensor(V, dtype=torch.float64).reshape(1, 1, V.shape[0], -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=sigma)
+    return o.reshape(-1).numpy()
+
+
+# ---------------------------------------------------------------------------
+# storage dtypes
+# ---------------------------------------------------------------------------
+def test_bf16_bit_patterns():
+    pats = np.array([0x3F80, 0xBF80, 0x4000, 0x3F00, 0x4049, 0x0001, 0x7F7F, 0x8000, 0x0080],
+                    dtype=np.uint16)
+    want = [1.0, -1.0, 2.0, 0.5, 3.140625, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127, -0.0,
+            2.0 ** -126]
+    got = O.upcast(pats, "bf16")
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w)
+
+
+def test_bf16_upcast_matches_torch():
+    bits = RNG.integers(0, 2 ** 16, size=4096, dtype=np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]          # finite patterns only
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
+    np.testing.assert_array_equal(O.upcast(bits, "bf16"), t.numpy())
+
+
+def test_round_to_bf16_ties_by_hand():
+    one = 1.0
+    cases = {
+        one + 2.0 ** -8: 0x3F80,                   # halfway 1 .. 1+2^-7 -> even (1.0)
+        one + 3 * 2.0 ** -8: 0x3F82,               # halfway 1+2^-7 .. 1+2^-6 -> even
+        one + 2.0 ** -8 + 2.0 ** -30: 0x3F81,      # just above the tie
+        -(one + 2.0 ** -8 - 2.0 ** -40): 0xBF80,   # just below the tie, negative
+        2.0 ** -133 * 0.5: 0x0000,                 # half the smallest subnormal -> even (0)
+        2.0 ** -133 * 1.5: 0x0002,                 # 1.5 ulp subnormal -> even (2 ulp)
+        0.0: 0x0000,
+    }
+    for v, bits in cases.items():
+        assert int(O.round_to_bf16_bits(np.array([v]))[0]) == bits, (v, hex(bits))
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    x = (RNG.standard_normal(20000) * np.exp(RNG.uniform(-30, 30, 20000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.round_to_bf16_bits(x.astype(np.float64)), want)
+
+
+def test_int8_dequant_exact():
+    codes = RNG.integers(-127, 128, size=(3, 5, 16)).astype(np.int8)
+    scales = (RNG.uniform(1e-4, 3.0, size=(3, 5))).astype(np.float16)
+    got = O.dequant_latent(codes, "i8", scales)
+    for idx in np.ndindex(codes.shape):
+        exact = Fraction(int(codes[idx])) * Fraction(float(scales[idx[:-1]]))
+        assert Fraction(got[idx]) == exact
+
+
+# ---------------------------------------------------------------------------
+# attention special cases
+# ---------------------------------------------------------------------------
+def test_identity_factor_is_textbook_attention():
+    """r = H and B = I: the method reduces to plain attention (library SDPA)."""
+    H, L = 16, 37
+    q = RNG.standard_normal((2, H))
+    CK = RNG.standard_normal((2, L, H))
+    CV = RNG.standard_normal((2, L, H))
+    I = np.stack([np.eye(H)] * 2)
+    inp = _inp_f64(q, CK, CV, I, I)
+    sigma = 1 / math.sqrt(H)
+    out = O.decode_attn(inp)
+    for h in range(2):
+        np.testing.assert_allclose(out[0, h], _sdpa(q[h], CK[h], CV[h], sigma), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("H,r", [(12, 5), (8, 8)])
+def test_scaled_selection_factor_reconstructs_by_indexing(H, r):
+    """B with one nonzero per row: K's columns are scaled copies of the
+    latent's columns (no matmul needed); then compare with library SDPA.
+    The square case uses a cyclic shift, so a transposed factor differs."""
+    L = 23
+    perm = (np.arange(r) + 1) % H if r == H else RNG.permutation(H)[:r]
+    d = RNG.uniform(0.5, 2.0, r) * RNG.choice([-1, 1], r)
+    BK = np.zeros((r, H)); BK[np.arange(r), perm] = d
+    perm2 = (np.arange(r) + 3) % H if r == H else RNG.permutation(H)[:r]
+    d2 = RNG.uniform(0.5, 2.0, r)
+    BV = np.zeros((r, H)); BV[np.arange(r), perm2] = d2
+    CK = RNG.standard_normal((1, L, r)); CV = RNG.standard_normal((1, L, r))
+    q = RNG.standard_normal((1, H))
+    K = np.zeros((L, H)); K[:, perm] = CK[0] * d
+    V = np.zeros((L, H)); V[:, perm2] = CV[0] * d2
+    inp = _inp_f64(q, CK, CV, BK[None], BV[None])
+    np.testing.assert_allclose(O.decode_attn(inp)[0, 0], _sdpa(q[0], K, V, 1 / math.sqrt(H)),
+                               rtol=0, atol=1e-13)
+
+
+def test_rank_one_closed_form():
+    """r = 1: k_t = c_t b, v_t = d_t g  =>  out = softmax(sigma c (b.q)) . d  * g."""
+    H, L = 8, 19
+    c = RNG.standard_normal(L); dv = RNG.standard_normal(L)
+    b = RNG.standard_normal(H); g = RNG.standard_normal(H); q = RNG.standard_normal(H)
+    sigma = 0.7
+    p = scipy.special.softmax(sigma * c * float(np.dot(b, q)))
+    want = float(np.dot(p, dv)) * g
+    inp = _inp_f64(q[None], c[None, :, None], dv[None, :, None], b[None, None, :], g[None, None, :])
+    np.testing.assert_allclose(O.decode_attn(inp, softmax_scale=sigma)[0, 0], want, atol=1e-14)
+
+
+def test_two_tokens_logistic():
+    H, r = 6, 3
+    BK = RNG.standard_normal((r, H)); BV = RNG.standard_normal((r, H))
+    CK = RNG.standard_normal((2, r)); CV = RNG.standard_normal((2, r))
+    q = RNG.standard_normal(H)
+    k0, k1 = [sum(CK[t, i] * BK[i] for i in range(r)) for t in (0, 1)]
+    v0, v1 = [sum(CV[t, i] * BV[i] for i in range(r)) for t in (0, 1)]
+    sigma = 1 / math.sqrt(H)
+    d = sigma * (float(np.dot(k0, q)) - float(np.dot(k1, q)))
+    want = scipy.special.expit(d) * v0 + scipy.special.expit(-d) * v1
+    inp = _inp_f64(q[None], CK[None], CV[None], BK[None], BV[None])
+    np.testing.assert_allclose(O.decode_attn(inp)[0, 0], want, atol=1e-14)
+
+
+def test_single_token_returns_its_value_row():
+    H, r = 10, 4
+    BV = RNG.standard_normal((r, H)); cv = RNG.standard_normal(r)
+    v0 = [sum(cv[i] * BV[i, j] for i in range(r)) for j in range(H)]
+    inp = _inp_f64(RNG.standard_normal((1, H)), RNG.standard_normal((1, 1, r)), cv[None, None, :],
+                   RNG.standard_normal((1, r, H)), BV[None])
+    np.testing.assert_allclose(O.decode_attn(inp)[0, 0], v0, rtol=0, atol=1e-14)
+
+
+def test_zero_query_gives_mean_value():
+    H, r, L = 10, 4, 29
+    BV = RNG.standard_normal((r, H)); CV = RNG.standard_normal((L, r))
+    mean = [sum(sum(CV[t, i] * BV[i, j] for i in range(r)) for t in range(L)) / L for j in range(H)]
+    inp = _inp_f64(np.zeros((1, H)), RNG.standard_normal((1, L, r)), CV[None],
+                   RNG.standard_normal((1, r, H)), BV[None])
+    np.testing.assert_allclose(O.decode_attn(inp)[0, 0], mean, atol=1e-14)
+
+
+def test_dominant_token_is_selected():
+    """One score 1000 above the rest: out is that token's value row, no overflow."""
+    H, L = 8, 50
+    I = np.eye(H)
+    CK = RNG.standard_normal((L, H)) * 0.1
+    CK[17] = 0.0; CK[17, 0] = 1000.0 * math.sqrt(H)
+    q = np.zeros(H); q[0] = 1.0
+    CV = RNG.standard_normal((L, H))
+    out = O.decode_attn(_inp_f64(q[None], CK[None], CV[None], I[None], I[None]))[0, 0]
+    np.testing.assert_allclose(out, CV[17], rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(out))
+
+
+def test_softmax_weights_sum_shift_and_overflow():
+    s = RNG.standard_normal(1000) * 5
+    p = O.softmax_weights(s)
+    assert abs(p.sum() - 1.0) < 1e-14 and np.all(p > 0)
+    np.testing.assert_allclose(O.softmax_weights(s + 1000.0), p, rtol=1e-12)
+    np.testing.assert_allclose(p, scipy.special.softmax(s), rtol=1e-13)
+    big = O.softmax_weights(s * 1e4)
+    assert np.all(np.isfinite(big)) and abs(big.sum() - 1) < 1e-14
+
+
+def test_token_permutation_invariance():
+    H, r, L = 16, 8, 41
+    inp = _inp_f64(RNG.standard_normal((1, H)), RNG.standard_normal((1, L, r)),
+                   RNG.standard_normal((1, L, r)), RNG.standard_normal((1, r, H)),
+                   RNG.standard_normal((1, r, H)))
+    perm = RNG.permutation(L)
+    inp2 = _inp_f64(inp.q[0], inp.C_K[0][:, perm], inp.C_V[0][:, perm], inp.B_K, inp.B_V)
+    np.testing.assert_allclose(O.decode_attn(inp2), O.decode_attn(inp), atol=1e-14)
+
+
+def test_hadamard_rotation_is_absorbed():
+    """c -> c S, B -> S^T B with S an orthonormal Hadamard leaves out unchanged."""
+    H, r, L = 32, 16, 33
+    S = scipy.linalg.hadamard(r) / math.sqrt(r)
+    CK = RNG.standard_normal((1, L, r)); CV = RNG.standard_normal((1, L, r))
+    BK = RNG.standard_normal((1, r, H)); BV = RNG.standard_normal((1, r, H))
+    q = RNG.standard_normal((1, H))
+    a = O.decode_attn(_inp_f64(q, CK, CV, BK, BV))
+    b = O.decode_attn(_inp_f64(q, (CK[0] @ S)[None], (CV[0] @ S)[None], (S.T @ BK[0])[None],
+                              (S.T @ BV[0])[None]))
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_factor_product_associativity():
+    """(c B) q == c (B q): reconstruct-then-dot equals the folded query."""
+    H, r, L = 24, 8, 15
+    c = RNG.standard_normal((L, r)); B = RNG.standard_normal((r, H)); q = RNG.standard_normal(H)
+    K = O.reconstruct(c, B)
+    qf = [sum(B[i, j] * q[j] for j in range(H)) for i in range(r)]
+    want = [sum(c[t, i] * qf[i] for i in range(r)) for t in range(L)]
+    np.testing.assert_allclose(K @ q, want, atol=1e-12)
+
+
+def test_brute_force_tiny():
+    """Everything in pure-Python loops with math.exp on a 2-head toy."""
+    nh, H, r, L = 2, 3, 2, 4
+    q = RNG.standard_normal((nh, H)); CK = RNG.standard_normal((nh, L, r))
+    CV = RNG.standard_normal((nh, L, r)); BK = RNG.standard_normal((nh, r, H))
+    BV = RNG.standard_normal((nh, r, H))
+    out = O.decode_attn(_inp_f64(q, CK, CV, BK, BV))
+    sig = 1 / math.sqrt(H)
+    for h in range(nh):
+        K = [[sum(CK[h, t, i] * BK[h, i, j] for i in range(r)) for j in range(H)] for t in range(L)]
+        V = [[sum(CV[h, t, i] * BV[h, i, j] for i in range(r)) for j in range(H)] for t in range(L)]
+        s = [sig * sum(K[t][j] * q[h, j] for j in range(H)) for t in range(L)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = sum(w)
+        o = [sum(w[t] * V[t][j] for t in range(L)) / z for j in range(H)]
+        np.testing.assert_allclose(out[0, h], o, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# splits and the merge
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ell,S", [(1, 1), (10, 1), (10, 2), (10, 3), (10, 7), (10, 10), (10, 13),
+                                   (1088, 8), (257, 4)])
+def test_split_bounds_partition(ell, S):
+    b = O.split_bounds(ell, S)
+    assert len(b) == S
+    covered = [t for (a, e) in b for t in range(a, e)]
+    assert covered == list(range(ell))
+    chunk = -(-ell // S)
+    assert all(e - a <= chunk for a, e in b)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 41, 50])
+def test_split_merge_equals_single_pass(S):
+    H, r, L = 16, 8, 41
+    q = RNG.standard_normal(H) * 3
+    K = RNG.standard_normal((L, r)) @ RNG.standard_normal((r, H))
+    V = RNG.standard_normal((L, r)) @ RNG.standard_normal((r, H))
+    parts = [O.segment_attend(q, K, V, 0.25, a, e) for a, e in O.split_bounds(L, S)]
+    o = np.array([p[0] for p in parts]); lse = np.array([p[1] for p in parts])
+    np.testing.assert_allclose(O.combine(o, lse), O.attend(q, K, V, 0.25), atol=1e-13)
+    # lse of the whole range, merged by log-sum-exp of the parts
+    s = 0.25 * (K @ q)
+    assert abs(scipy.special.logsumexp(lse[np.isfinite(lse)]) - scipy.special.logsumexp(s)) < 1e-12
+
+
+def test_segment_lse_is_logsumexp():
+    s_full = RNG.standard_normal(30)
+    K = np.eye(30); q = s_full.copy(); V = RNG.standard_normal((30, 4))
+    o, lse = O.segment_attend(q, K, V, 1.0, 5, 17)
+    assert abs(lse - scipy.special.logsumexp(s_full[5:17])) < 1e-13
+    np.testing.assert_allclose(o, scipy.special.softmax(s_full[5:17]) @ V[5:17], atol=1e-14)
+    o0, l0 = O.segment_attend(q, K, V, 1.0, 9, 9)
+    assert l0 == -math.inf and not o0.any()
+
+
+def test_combine_closed_forms():
+    a = RNG.standard_normal(5); b = RNG.standard_normal(5)
+    np.testing.assert_allclose(O.combine(np.stack([a, b]), np.array([2.0, 2.0])), (a + b) / 2, atol=1e-15)
+    np.testing.assert_allclose(O.combine(np.stack([a, b]), np.array([-math.inf, 7.0])), b, atol=0)
+    w = scipy.special.expit(1.5)   # lse difference 1.5 -> logistic weight
+    np.testing.assert_allclose(O.combine(np.stack([a, b]), np.array([1.5, 0.0])), w * a + (1 - w) * b,
+                               atol=1e-15)
+    assert not O.combine(np.stack([a, b]), np.array([-math.inf, -math.inf])).any()
+
+
+def test_zero_length_and_clamp():
+    H, r, L = 8, 4, 6
+    inp = _inp_f64(RNG.standard_normal((1, H)), RNG.standard_normal((1, L, r)),
+                   RNG.standard_normal((1, L, r)), RNG.standard_normal((1, r, H)),
+                   RNG.standard_normal((1, r, H)), L=[0])
+    assert not O.decode_attn(inp).any()
+    inp.L = np.array([L + 100], np.int32)
+    full = O.decode_attn(inp)
+    inp.L = np.array([L], np.int32)
+    np.testing.assert_array_equal(full, O.decode_attn(inp))
+
+
+def test_partials_of_decode_match_segments():
+    H, r, L = 16, 8, 23
+    inp = _inp_f64(RNG.standard_normal((1, H)), RNG.standard_normal((1, L, r)),
+                   RNG.standard_normal((1, L, r)), RNG.standard_normal((1, r, H)),
+                   RNG.standard_normal((1, r, H)))
+    o, lse = O.decode_partials_one(inp, 0, 0, 4)
+    np.testing.assert_allclose(O.combine(o, lse), O.decode_attn(inp)[0, 0], atol=1e-13)
+    assert O.split_bounds(L, 4) == [(0, 6), (6, 12), (12, 18), (18, 23)]
+
+
+# ---------------------------------------------------------------------------
+# append
+# ---------------------------------------------------------------------------
+def test_append_brute_force_and_associativity():
+    nb, E, nh, r, H = 3, 7, 2, 3, 5
+    x = RNG.standard_normal((nb, E)); A = RNG.standard_normal((E, nh * r))
+    c = O.append_latents(x, "f64", A, "f64", nh, r)
+    for b in range(nb):
+        for h in range(nh):
+            for i in range(r):
+                want = sum(x[b, e] * A[e, h * r + i] for e in range(E))
+                assert abs(c[b, h, i] - want) < 1e-13
+    B = RNG.standard_normal((r, H))
+    for h in range(nh):
+        np.testing.assert_allclose(c[:, h] @ B, x @ (A[:, h * r:(h + 1) * r] @ B), atol=1e-12)
+
+
+def test_apply_append_writes_rounded_row_at_pos():
+    from rank_kv_cache_flash_amd.inputs import make_ragged_step_inputs
+    inp = make_ragged_step_inputs(3, 2, 16, 8, 32, 4, 9, 12, seed=7)
+    CK, CV, cK, cV = O.apply_append(inp)
+    for b in range(3):
+        p = int(inp.pos[b])
+        assert p == inp.L[b] - 1
+        np.testing.assert_array_equal(CK[b, :, p], O.round_to_bf16_bits(cK[b]))
+        np.testing.assert_array_equal(np.delete(CK[b], p, axis=1), np.delete(inp.C_K[b], p, axis=1))
+        # rounded row within half a bf16 ulp of the exact latent
+        back = O.upcast(CK[b, :, p], "bf16")
+        ulp = np.ldexp(1.0, np.frexp(np.abs(cK[b]))[1] - 8)
+        assert np.all(np.abs(back - cK[b]) <= ulp / 2 + 1e-300)
