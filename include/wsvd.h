@@ -1,0 +1,198 @@
+/*
+ * wsvd.h -- C ABI of libwsvd.so: WSVD per-head low-rank flash decoding on
+ * AMD MI355X (gfx950).
+ *
+ * Citations refer to the page "WSVD: Weighted Low-Rank Approximation for
+ * Fast and Efficient Execution of Low-Precision Vision-Language Models"
+ * (gist.science, paper 2604.02570) by language and section.
+ *
+ * Notation (Arabic page section 2a; German page section 2A): head h of an
+ * attention layer factors its key projection as W_Kh ~ A_Kh B_Kh with
+ * A_Kh in R^{E x r} and B_Kh in R^{r x H}; E is the embedding width, H the
+ * head dimension and r the per-head rank.  The cache keeps, per head and
+ * per token, only the r-dim latent C_Kh = x A_Kh (L x r per head).  Values
+ * are factored the same way (A_Vh, B_Vh, C_Vh).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer is a caller-owned DEVICE buffer unless stated otherwise.
+ *   The library allocates nothing and keeps no state: calls are reentrant
+ *   and may be issued from several host threads on different streams.
+ * - Tensors are dense and row-major with the shapes given below.  Every
+ *   tensor base pointer must be 16-byte aligned (torch allocations are).
+ * - Calls only enqueue work on `stream` and return; nothing synchronises.
+ *   Outputs are valid once the stream reaches that point.
+ * - Every argument problem that the host can see is reported by a negative
+ *   wsvd_status before anything is launched: NULL pointers, non-positive
+ *   sizes, r > H, an (H, r, dtype) combination that is not compiled,
+ *   misaligned pointers, a workspace that is too small.  A failed launch
+ *   returns WSVD_ERR_HIP.  There is no fallback path.
+ * - Values held in device memory (L[b], pos[b]) cannot be checked by the
+ *   host; their documented handling is below.
+ * - Compiled shapes: H in {64, 128}; r in {16, 32, 48, 64} with r <= H.
+ */
+#ifndef WSVD_H_
+#define WSVD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wsvd_dtype {
+    WSVD_F32 = 0,   /* IEEE binary32                                  */
+    WSVD_BF16 = 1,  /* bfloat16 (upper half of a binary32)            */
+    WSVD_F16 = 2,   /* IEEE binary16 (only for q, B, x, A and out)    */
+    WSVD_I8 = 3     /* signed 8-bit codes (latent caches only)        */
+} wsvd_dtype;
+
+typedef enum wsvd_status {
+    WSVD_OK = 0,
+    WSVD_ERR_NULL = -1,         /* a required pointer is NULL                      */
+    WSVD_ERR_SHAPE = -2,        /* non-positive size, r > H, inconsistent sizes    */
+    WSVD_ERR_DTYPE = -3,        /* dtype not allowed for that argument             */
+    WSVD_ERR_UNSUPPORTED = -4,  /* (H, r, dtype) combination not compiled          */
+    WSVD_ERR_ALIGN = -5,        /* a base pointer is not 16-byte aligned           */
+    WSVD_ERR_WORKSPACE = -6,    /* workspace NULL or smaller than required         */
+    WSVD_ERR_HIP = -7           /* the HIP runtime reported a launch error         */
+} wsvd_status;
+
+/*
+ * wsvd_decode_attn -- one decode step of attention over a per-head latent
+ * cache, without materialising K or V.
+ *
+ * Defines (German page section 2D; Italian page section 2D; Arabic page
+ * section 2c; Japanese page section 2.4): latent tiles are streamed from
+ * memory, combined on chip with the head's factor, and used at once for
+ * qK^T, softmax and the V product inside a Flash-Decoding pass.  The result
+ * equals, for every sequence b and head h with l = L[b]:
+ *
+ *     K = C_K[b,h,:l,:] B_K[h],  V = C_V[b,h,:l,:] B_V[h]     (l x H)
+ *     out[b,h,:] = softmax(sigma * K q[b,h,:]) V
+ *
+ * computed here as q' = B_K[h] q (folded once), scores = C_K q', and an
+ * r-dim V accumulation projected through B_V[h] once per split.
+ *
+ * Arguments
+ *   nb, nh, H, r     batch, heads, head dim, per-head rank (> 0, r <= H)
+ *   L_cap            cache capacity in tokens (> 0)
+ *   L                int32 [nb]: tokens attended per sequence.  Device
+ *                    values are clamped to [0, L_cap]; L[b] == 0 yields a
+ *                    zero output row.
+ *   q, q_dt          [nb, nh, H]   F32 | BF16 | F16
+ *   C_K, C_V, C_dt   [nb, nh, L_cap, r]   F32 | BF16 | I8
+ *   s_K, s_V         fp16 [nb, nh, L_cap] per-token scales, required iff
+ *                    C_dt == WSVD_I8 (value = code * scale); else ignored
+ *   B_K, B_V, B_dt   [nh, r, H]    F32 | BF16 | F16
+ *   softmax_scale    sigma; <= 0 selects 1/sqrt(H)
+ *   n_splits         splits of each sequence (0 = automatic, see
+ *                    wsvd_decode_num_splits).  Split s of a sequence with
+ *                    l tokens covers [s*ceil(l/S), min(l, (s+1)*ceil(l/S))).
+ *   workspace        device scratch of at least wsvd_decode_workspace_bytes
+ *                    bytes, 256-byte aligned.  On return (stream order) it
+ *                    holds the split partials:
+ *                      o_part   float [nb, nh, S, H] at byte offset 0,
+ *                               each split's attention normalised over its
+ *                               own tokens (zeros for an empty split);
+ *                      lse_part float [nb, nh, S] at byte offset
+ *                               wsvd_decode_lse_offset(...): natural-log
+ *                               log-sum-exp of the split's scaled scores
+ *                               (-inf for an empty split).
+ *   out, out_dt      [nb, nh, H] F32 | BF16 | F16, or NULL to stop after the
+ *                    partials (e.g. to merge partials from several devices
+ *                    with wsvd_combine_splits).
+ *   stream           HIP stream to enqueue on (0 = null stream).
+ */
+int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap,
+                     const int32_t* L,
+                     const void* q, wsvd_dtype q_dt,
+                     const void* C_K, const void* C_V, wsvd_dtype C_dt,
+                     const uint16_t* s_K, const uint16_t* s_V,
+                     const void* B_K, const void* B_V, wsvd_dtype B_dt,
+                     float softmax_scale, int n_splits,
+                     void* workspace, size_t workspace_bytes,
+                     void* out, wsvd_dtype out_dt,
+                     hipStream_t stream);
+
+/*
+ * wsvd_combine_splits -- merge per-split partials into the attention output.
+ *
+ * The Flash-Decoding pass named on the German page section 2D (and the
+ * Japanese page section 2.4) splits the cached tokens; this is its merge:
+ * out = sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max_s lse_s).
+ * Splits with lse = -inf carry no weight; if every split of a row is empty
+ * the row is zero.  Rounding to out_dt is to nearest, ties to even.
+ *
+ *   o_part   float [nb, nh, S, H]  (S = n_splits > 0)
+ *   lse_part float [nb, nh, S]
+ *   out      [nb, nh, H] in out_dt (F32 | BF16 | F16)
+ */
+int wsvd_combine_splits(int nb, int nh, int H, int n_splits,
+                        const float* o_part, const float* lse_part,
+                        void* out, wsvd_dtype out_dt,
+                        hipStream_t stream);
+
+/*
+ * wsvd_append_latent -- project the new token of each sequence to its
+ * per-head latents and write them into the caches.
+ *
+ * Per head, the cached latent is the token activation times the head's
+ * factor A_Kh in R^{E x r} (Arabic page section 2a; German page section 2A;
+ * Japanese page section 2.1).  For every b and h:
+ *
+ *     C_K[b, h, pos[b], :] = x[b, :] A_K[:, h*r:(h+1)*r]
+ *     C_V[b, h, pos[b], :] = x[b, :] A_V[:, h*r:(h+1)*r]
+ *
+ * accumulated in fp32 on matrix cores and rounded once to C_dt (nearest,
+ * ties to even).  Only C_dt == WSVD_BF16 or WSVD_F32 caches are written by
+ * this version (WSVD_I8 returns WSVD_ERR_UNSUPPORTED).
+ *
+ *   nb, E, nh, r     batch, embedding width, heads, rank (r as above)
+ *   L_cap            cache capacity in tokens
+ *   x, x_dt          [nb, E]         BF16
+ *   A_K, A_V, A_dt   [E, nh*r]       BF16 (column block h is A_Kh)
+ *   pos              int32 [nb] device: row to write; rows with pos[b]
+ *                    outside [0, L_cap) are skipped
+ *   C_K, C_V, C_dt   [nb, nh, L_cap, r]
+ *   s_K, s_V         unused (must be NULL) for BF16/F32 caches
+ *   workspace        device scratch of wsvd_append_workspace_bytes(...)
+ *                    bytes (fp32 split-E partial products), 256-byte aligned
+ */
+int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap,
+                       const void* x, wsvd_dtype x_dt,
+                       const void* A_K, const void* A_V, wsvd_dtype A_dt,
+                       const int32_t* pos,
+                       void* C_K, void* C_V, wsvd_dtype C_dt,
+                       uint16_t* s_K, uint16_t* s_V,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Splits wsvd_decode_attn uses for these sizes (n_splits > 0 is returned
+ * unchanged; 0 selects the automatic choice).  Pure host function.
+ * Returns a negative wsvd_status for invalid sizes. */
+int wsvd_decode_num_splits(int nb, int nh, int L_cap, int n_splits);
+
+/* Workspace bytes wsvd_decode_attn needs (0 on invalid sizes).  Pure host. */
+size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_splits);
+
+/* Byte offset of lse_part inside the decode workspace.  Pure host. */
+size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits);
+
+/* Workspace bytes wsvd_append_latent needs (0 on invalid sizes).  Pure host. */
+size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r);
+
+/* Static description of a status code.  Pure host; never NULL. */
+const char* wsvd_status_string(int status);
+
+/* Library version, e.g. "wsvd 0.1 gfx950".  Pure host. */
+const char* wsvd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WSVD_H_ */

@@ -1,0 +1,179 @@
+// abi.hip -- the C entry points declared in include/wsvd.h.
+//
+// Every check that the host can make happens here, before any HIP call, so
+// a bad argument returns a negative status with nothing enqueued (and these
+// paths work on a machine without a GPU).  Kernels live in decode.hip,
+// combine.hip and append.hip.
+#include <stdint.h>
+#include <string.h>
+
+#include "wsvd_common.hpp"
+#include "wsvd_internal.hpp"
+
+namespace {
+
+constexpr int kTargetBlocks = 2048;  // ~8 split blocks per CU on 256 CUs
+constexpr int kMinSplitTokens = 128; // below this a split's fixed cost dominates
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool act_dtype_ok(int dt) { return dt == WSVD_F32 || dt == WSVD_BF16 || dt == WSVD_F16; }
+bool cache_dtype_ok(int dt) { return dt == WSVD_F32 || dt == WSVD_BF16 || dt == WSVD_I8; }
+bool head_dim_ok(int H) { return H == 64 || H == 128; }
+bool rank_ok(int r) { return r == 16 || r == 32 || r == 48 || r == 64; }
+
+int resolve_splits(int nb, int nh, int L_cap, int n_splits) {
+    if (nb <= 0 || nh <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
+    if (n_splits > 0) return n_splits > L_cap ? WSVD_ERR_SHAPE : n_splits;
+    const long bh = (long)nb * nh;
+    long s = (kTargetBlocks + bh - 1) / bh;
+    const long smax = (L_cap + kMinSplitTokens - 1) / kMinSplitTokens;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t opart_bytes(int nb, int nh, int H, int S) { return (size_t)nb * nh * S * H * sizeof(float); }
+
+}  // namespace
+
+extern "C" {
+
+int wsvd_decode_num_splits(int nb, int nh, int L_cap, int n_splits) {
+    return resolve_splits(nb, nh, L_cap, n_splits);
+}
+
+size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits) {
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0 || H <= 0) return 0;
+    return round_up(opart_bytes(nb, nh, H, S), 256);
+}
+
+size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_splits) {
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0 || H <= 0) return 0;
+    return round_up(opart_bytes(nb, nh, H, S), 256) + round_up((size_t)nb * nh * S * sizeof(float), 256);
+}
+
+size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r) {
+    if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0) return 0;
+    const int ks = wsvd::append_num_esplits(nb, E, nh, r);
+    return round_up((size_t)ks * nb * 2 * nh * r * sizeof(float), 256);
+}
+
+const char* wsvd_status_string(int st) {
+    switch (st) {
+        case WSVD_OK: return "ok";
+        case WSVD_ERR_NULL: return "a required pointer is NULL";
+        case WSVD_ERR_SHAPE: return "invalid or inconsistent sizes";
+        case WSVD_ERR_DTYPE: return "dtype not allowed for this argument";
+        case WSVD_ERR_UNSUPPORTED: return "shape/dtype combination not compiled";
+        case WSVD_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case WSVD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case WSVD_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+const char* wsvd_version(void) { return "wsvd 0.1 gfx950"; }
+
+int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, const void* q, wsvd_dtype q_dt,
+                     const void* C_K, const void* C_V, wsvd_dtype C_dt, const uint16_t* s_K, const uint16_t* s_V,
+                     const void* B_K, const void* B_V, wsvd_dtype B_dt, float softmax_scale, int n_splits,
+                     void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt, hipStream_t stream) {
+    if (nb <= 0 || nh <= 0 || H <= 0 || r <= 0 || L_cap <= 0 || n_splits < 0 || r > H) return WSVD_ERR_SHAPE;
+    if ((long long)nb * nh * L_cap * r > (1ll << 46)) return WSVD_ERR_SHAPE;
+    if (!L || !q || !C_K || !C_V || !B_K || !B_V) return WSVD_ERR_NULL;
+    if (!act_dtype_ok(q_dt) || !act_dtype_ok(B_dt) || !cache_dtype_ok(C_dt)) return WSVD_ERR_DTYPE;
+    if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
+    if (C_dt == WSVD_I8 && (!s_K || !s_V)) return WSVD_ERR_NULL;
+    if (!head_dim_ok(H) || !rank_ok(r)) return WSVD_ERR_UNSUPPORTED;
+    if (!aligned16(L) || !aligned16(q) || !aligned16(C_K) || !aligned16(C_V) || !aligned16(B_K) ||
+        !aligned16(B_V) || (out && !aligned16(out)))
+        return WSVD_ERR_ALIGN;
+    if (C_dt == WSVD_I8 && (!aligned16(s_K) || !aligned16(s_V))) return WSVD_ERR_ALIGN;
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0) return WSVD_ERR_SHAPE;
+    if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+
+    wsvd::DecodeArgs a;
+    a.nb = nb;
+    a.nh = nh;
+    a.L_cap = L_cap;
+    a.S = S;
+    a.L = L;
+    a.q = q;
+    a.q_dt = q_dt;
+    a.C_K = C_K;
+    a.C_V = C_V;
+    a.s_K = C_dt == WSVD_I8 ? s_K : nullptr;
+    a.s_V = C_dt == WSVD_I8 ? s_V : nullptr;
+    a.B_K = B_K;
+    a.B_V = B_V;
+    a.B_dt = B_dt;
+    const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
+    a.scale_log2 = sigma * wsvd::kLog2e;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
+
+    if (wsvd::launch_decode_split(a, H, r, C_dt, stream) != hipSuccess) return WSVD_ERR_HIP;
+    if (out) {
+        if (wsvd::launch_combine(nb, nh, H, S, a.o_part, a.lse_part, out, out_dt, stream) != hipSuccess)
+            return WSVD_ERR_HIP;
+    }
+    return WSVD_OK;
+}
+
+int wsvd_combine_splits(int nb, int nh, int H, int n_splits, const float* o_part, const float* lse_part, void* out,
+                        wsvd_dtype out_dt, hipStream_t stream) {
+    if (nb <= 0 || nh <= 0 || H <= 0 || n_splits <= 0) return WSVD_ERR_SHAPE;
+    if (!o_part || !lse_part || !out) return WSVD_ERR_NULL;
+    if (!act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
+    if (!head_dim_ok(H)) return WSVD_ERR_UNSUPPORTED;
+    if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(out)) return WSVD_ERR_ALIGN;
+    if ((long long)nb * nh >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    return wsvd::launch_combine(nb, nh, H, n_splits, o_part, lse_part, out, out_dt, stream) == hipSuccess
+               ? WSVD_OK
+               : WSVD_ERR_HIP;
+}
+
+int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, wsvd_dtype x_dt, const void* A_K,
+                       const void* A_V, wsvd_dtype A_dt, const int32_t* pos, void* C_K, void* C_V, wsvd_dtype C_dt,
+                       uint16_t* s_K, uint16_t* s_V, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0 || L_cap <= 0) return WSVD_ERR_SHAPE;
+    if (!x || !A_K || !A_V || !pos || !C_K || !C_V) return WSVD_ERR_NULL;
+    if (x_dt != WSVD_BF16 || A_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
+    if (!cache_dtype_ok(C_dt)) return WSVD_ERR_DTYPE;
+    if (C_dt == WSVD_I8) return WSVD_ERR_UNSUPPORTED;
+    if (s_K || s_V) return WSVD_ERR_SHAPE;
+    if (!rank_ok(r) || E % 256 != 0) return WSVD_ERR_UNSUPPORTED;
+    if ((long long)nb * nh * L_cap * r > (1ll << 46) || (long long)E * nh * r > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(A_K) || !aligned16(A_V) || !aligned16(pos) || !aligned16(C_K) ||
+        !aligned16(C_V))
+        return WSVD_ERR_ALIGN;
+    const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+
+    wsvd::AppendArgs a;
+    a.nb = nb;
+    a.E = E;
+    a.nh = nh;
+    a.r = r;
+    a.L_cap = L_cap;
+    a.x = static_cast<const uint16_t*>(x);
+    a.A_K = static_cast<const uint16_t*>(A_K);
+    a.A_V = static_cast<const uint16_t*>(A_V);
+    a.pos = pos;
+    a.C_K = C_K;
+    a.C_V = C_V;
+    a.C_dt = C_dt;
+    a.part = static_cast<float*>(workspace);
+    a.KS = wsvd::append_num_esplits(nb, E, nh, r);
+    return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
+}  // extern "C"

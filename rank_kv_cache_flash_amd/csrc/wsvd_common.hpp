@@ -1,0 +1,96 @@
+// wsvd_common.hpp -- shared device helpers for the gfx950 kernels.
+//
+// Only what several kernels need: dtype conversions, DPP row reductions
+// and small vector types.  Nothing here is used by the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wsvd.h"
+
+namespace wsvd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+__device__ __forceinline__ float f16_to_f32(uint16_t v) {
+    return (float)__builtin_bit_cast(_Float16, v);
+}
+
+// float -> bf16, round to nearest, ties to even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // nearest, ties to even
+}
+
+// Element `i` of a q / B / x / A style tensor of runtime dtype `dt`, as float.
+__device__ __forceinline__ float load_elem(const void* p, int dt, size_t i) {
+    switch (dt) {
+        case WSVD_F32: return static_cast<const float*>(p)[i];
+        case WSVD_BF16: return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+        default: return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+}
+
+__device__ __forceinline__ void store_elem(void* p, int dt, size_t i, float v) {
+    switch (dt) {
+        case WSVD_F32: static_cast<float*>(p)[i] = v; break;
+        case WSVD_BF16: static_cast<uint16_t*>(p)[i] = f32_to_bf16(v); break;
+        default: static_cast<uint16_t*>(p)[i] = f32_to_f16(v); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane sums inside rows of 16 lanes (DPP: no LDS traffic)
+// ---------------------------------------------------------------------------
+// DPP control words (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane j of 8 <-> 7-j
+constexpr int kDppRowMirror = 0x140;   // lane j of 16 <-> 15-j
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of a
+// group ends with the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp_f<kDppQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp_f<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+    return __shfl_xor(v, m, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load marked non-temporal: the latent stream is read once,
+// so it should not evict the factor lines that many workgroups reuse.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+
+}  // namespace wsvd

@@ -1,0 +1,52 @@
+// wsvd_internal.hpp -- argument blocks and launchers shared by the C ABI
+// (abi.hip) and the kernel files.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wsvd {
+
+// Everything the split decode kernel reads, passed by value as kernargs.
+struct DecodeArgs {
+    int nb, nh, L_cap, S;
+    const int32_t* L;
+    const void* q;
+    int q_dt;
+    const void* C_K;
+    const void* C_V;
+    const uint16_t* s_K;
+    const uint16_t* s_V;
+    const void* B_K;
+    const void* B_V;
+    int B_dt;
+    float scale_log2;  // softmax scale times log2(e)
+    float* o_part;     // [nb, nh, S, H]
+    float* lse_part;   // [nb, nh, S]
+};
+
+hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipStream_t st);
+
+hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, const float* lse_part,
+                          void* out, int out_dt, hipStream_t st);
+
+struct AppendArgs {
+    int nb, E, nh, r, L_cap;
+    const uint16_t* x;    // bf16 [nb, E]
+    const uint16_t* A_K;  // bf16 [E, nh*r]
+    const uint16_t* A_V;
+    const int32_t* pos;
+    void* C_K;
+    void* C_V;
+    int C_dt;
+    float* part;          // fp32 [KS, nb, 2*nh*r] split-E partial products
+    int KS;               // number of E splits
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+// Split-E factor the append kernel uses for these sizes (host).
+int append_num_esplits(int nb, int E, int nh, int r);
+
+}  // namespace wsvd

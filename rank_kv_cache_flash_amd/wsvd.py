@@ -1,0 +1,220 @@
+"""Python binding of libwsvd.so: torch tensors in, the same C calls out.
+
+Argument marshalling only -- every step of the decode runs in the HIP
+kernels behind include/wsvd.h.  Tensors must already live on the GPU;
+there is no CPU path and a missing library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwsvd.so")
+
+F32, BF16, F16, I8 = 0, 1, 2, 3
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8}
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16, I8: torch.int8}
+
+_lib = None
+
+
+class WsvdError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwsvd.so once (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rank_kv_cache_flash_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.wsvd_decode_attn.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32,
+                                   f32, i32, vp, sz, vp, i32, vp]
+    L.wsvd_decode_attn.restype = i32
+    L.wsvd_combine_splits.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
+    L.wsvd_combine_splits.restype = i32
+    L.wsvd_append_latent.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, vp,
+                                     vp, sz, vp]
+    L.wsvd_append_latent.restype = i32
+    L.wsvd_decode_num_splits.argtypes = [i32, i32, i32, i32]
+    L.wsvd_decode_num_splits.restype = i32
+    L.wsvd_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.wsvd_decode_workspace_bytes.restype = sz
+    L.wsvd_decode_lse_offset.argtypes = [i32, i32, i32, i32, i32]
+    L.wsvd_decode_lse_offset.restype = sz
+    L.wsvd_append_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.wsvd_append_workspace_bytes.restype = sz
+    L.wsvd_status_string.argtypes = [i32]
+    L.wsvd_status_string.restype = ctypes.c_char_p
+    L.wsvd_version.argtypes = []
+    L.wsvd_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().wsvd_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().wsvd_version().decode()
+
+
+def decode_num_splits(nb, nh, L_cap, n_splits=0) -> int:
+    return int(lib().wsvd_decode_num_splits(nb, nh, L_cap, n_splits or 0))
+
+
+def decode_workspace_bytes(nb, nh, H, L_cap, n_splits=0) -> int:
+    return int(lib().wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits or 0))
+
+
+def decode_lse_offset(nb, nh, H, L_cap, n_splits=0) -> int:
+    return int(lib().wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits or 0))
+
+
+def append_workspace_bytes(nb, E, nh, r) -> int:
+    return int(lib().wsvd_append_workspace_bytes(nb, E, nh, r))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(st, call):
+    if st != 0:
+        raise WsvdError(st, call)
+
+
+def decode_attn(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=None, n_splits=None,
+                out=None, out_dtype=None, workspace=None, partials_only=False, stream=None):
+    """wsvd_decode_attn on torch tensors.
+
+    q [nb, nh, H]; C_K / C_V [nb, nh, L_cap, r]; B_K / B_V [nh, r, H];
+    L int32 [nb] (device); s_K / s_V fp16 [nb, nh, L_cap] for int8 caches.
+    Returns out [nb, nh, H] (or None with partials_only) and the partial
+    views (o_part [nb, nh, S, H], lse_part [nb, nh, S]) inside workspace.
+    """
+    for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"),
+                 (s_K, "s_K"), (s_V, "s_V"), (out, "out"), (workspace, "workspace")):
+        _dev(t, n)
+    nb, nh, H = q.shape
+    L_cap, r = C_K.shape[2], C_K.shape[3]
+    S = decode_num_splits(nb, nh, L_cap, n_splits or 0)
+    if S <= 0:
+        raise WsvdError(S, "wsvd_decode_num_splits")
+    need = decode_workspace_bytes(nb, nh, H, L_cap, n_splits or 0)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if not partials_only and out is None:
+        out = torch.empty((nb, nh, H), dtype=out_dtype or q.dtype, device=q.device)
+    if partials_only:
+        out = None
+    if s_K is not None and s_K.dtype == torch.float16:
+        s_K = s_K.view(torch.int16)
+    if s_V is not None and s_V.dtype == torch.float16:
+        s_V = s_V.view(torch.int16)
+    st = lib().wsvd_decode_attn(
+        nb, nh, H, r, L_cap, _ptr(L), _ptr(q), _DT[q.dtype], _ptr(C_K), _ptr(C_V), _DT[C_K.dtype],
+        _ptr(s_K), _ptr(s_V), _ptr(B_K), _ptr(B_V), _DT[B_K.dtype],
+        float(softmax_scale or 0.0), int(n_splits or 0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(out), _DT[out.dtype] if out is not None else 0, _stream(stream))
+    _check(st, "wsvd_decode_attn")
+    off = decode_lse_offset(nb, nh, H, L_cap, n_splits or 0)
+    wsb = workspace.view(torch.uint8).reshape(-1)
+    o_part = wsb[: nb * nh * S * H * 4].view(torch.float32).view(nb, nh, S, H)
+    lse_part = wsb[off: off + nb * nh * S * 4].view(torch.float32).view(nb, nh, S)
+    return out, o_part, lse_part
+
+
+def combine_splits(o_part, lse_part, *, out=None, out_dtype=torch.float32, stream=None):
+    """wsvd_combine_splits: o_part [nb, nh, S, H] fp32, lse_part [nb, nh, S] fp32."""
+    _dev(o_part, "o_part"); _dev(lse_part, "lse_part"); _dev(out, "out")
+    nb, nh, S, H = o_part.shape
+    if out is None:
+        out = torch.empty((nb, nh, H), dtype=out_dtype, device=o_part.device)
+    st = lib().wsvd_combine_splits(nb, nh, H, S, _ptr(o_part), _ptr(lse_part), _ptr(out), _DT[out.dtype],
+                                   _stream(stream))
+    _check(st, "wsvd_combine_splits")
+    return out
+
+
+def append_latent(x, A_K, A_V, pos, C_K, C_V, *, workspace=None, stream=None):
+    """wsvd_append_latent: x [nb, E] bf16, A_K / A_V [E, nh*r] bf16, pos int32 [nb],
+    caches [nb, nh, L_cap, r] written in place at row pos[b]."""
+    for t, n in ((x, "x"), (A_K, "A_K"), (A_V, "A_V"), (pos, "pos"), (C_K, "C_K"), (C_V, "C_V"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    nb, E = x.shape
+    _, nh, L_cap, r = C_K.shape
+    need = append_workspace_bytes(nb, E, nh, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib().wsvd_append_latent(nb, E, nh, r, L_cap, _ptr(x), _DT[x.dtype], _ptr(A_K), _ptr(A_V), _DT[A_K.dtype],
+                                  _ptr(pos), _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], None, None, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "wsvd_append_latent")
+    return C_K, C_V
+
+
+# ---------------------------------------------------------------------------
+# host arrays (storage dtypes from rank_kv_cache_flash_amd.inputs) -> device
+# ---------------------------------------------------------------------------
+def to_device(arr, dt: str, device="cuda"):
+    """NumPy array in a storage dtype ('f32', 'bf16' bits, 'f16', 'i8', int32) -> GPU tensor."""
+    import numpy as np
+    if dt == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dt == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float16))
+    elif dt == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    elif dt == "i8":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int8))
+    elif dt == "i32":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int32))
+    else:
+        raise ValueError(dt)
+    return t.to(device)
+
+
+def device_inputs(inp, device="cuda"):
+    """All tensors of a DecodeInputs on the GPU, keyed like the binding's arguments."""
+    d = dict(
+        q=to_device(inp.q, inp.q_dt, device),
+        C_K=to_device(inp.C_K, inp.C_dt, device),
+        C_V=to_device(inp.C_V, inp.C_dt, device),
+        B_K=to_device(inp.B_K, inp.B_dt, device),
+        B_V=to_device(inp.B_V, inp.B_dt, device),
+        L=to_device(inp.L, "i32", device),
+    )
+    if inp.s_K is not None:
+        d["s_K"] = to_device(inp.s_K, "f16", device)
+        d["s_V"] = to_device(inp.s_V, "f16", device)
+    if inp.x is not None:
+        d["x"] = to_device(inp.x, inp.x_dt, device)
+        d["A_K"] = to_device(inp.A_K, inp.A_dt, device)
+        d["A_V"] = to_device(inp.A_V, inp.A_dt, device)
+        d["pos"] = to_device(inp.pos, "i32", device)
+    return d

@@ -1,0 +1,143 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status before launching.
+
+No call here reaches a kernel: each error case fails host validation, which
+runs before any HIP call, so these tests need no GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from rank_kv_cache_flash_amd import wsvd  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wsvd.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16, F16, I8 = 0, 1, 2, 3
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wsvd_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wsvd.LIB_PATH):
+        pytest.fail("libwsvd.so is not built (python -m rank_kv_cache_flash_amd.build)")
+    return wsvd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert {"wsvd_decode_attn", "wsvd_append_latent", "wsvd_combine_splits"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in wsvd.h but not exported"
+
+
+def test_status_strings_and_version(L):
+    for st in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EWS, EHIP, -99):
+        assert wsvd.status_string(st)
+    assert "gfx950" in wsvd.version()
+
+
+def test_split_rule_and_workspace_sizes(L):
+    assert wsvd.decode_num_splits(1, 32, 1088, 5) == 5
+    assert wsvd.decode_num_splits(1, 32, 1088, 0) >= 1
+    assert wsvd.decode_num_splits(0, 32, 1088, 0) == ESHAPE
+    assert wsvd.decode_num_splits(1, 32, 10, 11) == ESHAPE
+    for (nb, nh, H, Lc, S) in [(1, 4, 64, 256, 3), (16, 32, 128, 4096, 0), (2, 3, 64, 100, 7)]:
+        s = wsvd.decode_num_splits(nb, nh, Lc, S)
+        off = wsvd.decode_lse_offset(nb, nh, H, Lc, S)
+        ws = wsvd.decode_workspace_bytes(nb, nh, H, Lc, S)
+        assert off >= nb * nh * s * H * 4 and off % 256 == 0
+        assert ws >= off + nb * nh * s * 4
+    assert wsvd.decode_workspace_bytes(0, 1, 64, 1, 0) == 0
+    assert wsvd.append_workspace_bytes(64, 4096, 32, 48) % 256 == 0
+    assert wsvd.append_workspace_bytes(64, 4096, 32, 48) >= 64 * 2 * 32 * 48 * 4
+
+
+# fake, well-aligned device addresses: validation must reject before use
+P = 0x7F0000000000
+WS = 1 << 24
+
+
+def decode(L, **kw):
+    a = dict(nb=1, nh=4, H=64, r=16, L_cap=256, Lp=P, q=P, q_dt=F32, C_K=P, C_V=P, C_dt=F32, s_K=None,
+             s_V=None, B_K=P, B_V=P, B_dt=F32, scale=0.0, S=0, ws=P, ws_bytes=WS, out=P, out_dt=F32)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return L.wsvd_decode_attn(a["nb"], a["nh"], a["H"], a["r"], a["L_cap"], v(a["Lp"]), v(a["q"]), a["q_dt"],
+                              v(a["C_K"]), v(a["C_V"]), a["C_dt"], v(a["s_K"]), v(a["s_V"]), v(a["B_K"]),
+                              v(a["B_V"]), a["B_dt"], a["scale"], a["S"], v(a["ws"]), a["ws_bytes"], v(a["out"]),
+                              a["out_dt"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), ESHAPE), (dict(nh=-1), ESHAPE), (dict(H=0), ESHAPE), (dict(L_cap=0), ESHAPE),
+    (dict(r=128), ESHAPE), (dict(S=-1), ESHAPE), (dict(S=257), ESHAPE),
+    (dict(Lp=None), ENULL), (dict(q=None), ENULL), (dict(C_K=None), ENULL), (dict(C_V=None), ENULL),
+    (dict(B_K=None), ENULL), (dict(B_V=None), ENULL),
+    (dict(C_dt=I8), ENULL), (dict(C_dt=I8, s_K=P), ENULL),
+    (dict(q_dt=I8), EDTYPE), (dict(B_dt=7), EDTYPE), (dict(C_dt=F16), EDTYPE), (dict(out_dt=I8), EDTYPE),
+    (dict(H=96), EUNSUP), (dict(r=24), EUNSUP), (dict(H=256, r=16), EUNSUP), (dict(r=8), EUNSUP),
+    (dict(q=P + 8), EALIGN), (dict(C_K=P + 4), EALIGN), (dict(B_V=P + 2), EALIGN), (dict(out=P + 8), EALIGN),
+    (dict(C_dt=I8, s_K=P, s_V=P + 2), EALIGN), (dict(Lp=P + 4), EALIGN),
+    (dict(ws=None), EWS), (dict(ws_bytes=16), EWS), (dict(ws=P + 16), EWS),
+])
+def test_decode_rejects(L, kw, want):
+    assert decode(L, **kw) == want
+
+
+def test_decode_workspace_boundary(L):
+    need = wsvd.decode_workspace_bytes(1, 4, 64, 256, 3)
+    assert decode(L, S=3, ws_bytes=need - 1) == EWS
+
+
+def test_combine_rejects(L):
+    v = ctypes.c_void_p
+    f = L.wsvd_combine_splits
+    assert f(0, 1, 64, 2, v(P), v(P), v(P), F32, None) == ESHAPE
+    assert f(1, 1, 64, 0, v(P), v(P), v(P), F32, None) == ESHAPE
+    assert f(1, 1, 64, 2, None, v(P), v(P), F32, None) == ENULL
+    assert f(1, 1, 64, 2, v(P), v(P), None, F32, None) == ENULL
+    assert f(1, 1, 64, 2, v(P), v(P), v(P), I8, None) == EDTYPE
+    assert f(1, 1, 96, 2, v(P), v(P), v(P), F32, None) == EUNSUP
+    assert f(1, 1, 64, 2, v(P + 4), v(P), v(P), F32, None) == EALIGN
+
+
+def append(L, **kw):
+    a = dict(nb=64, E=4096, nh=32, r=48, L_cap=8192, x=P, x_dt=BF16, A_K=P, A_V=P, A_dt=BF16, pos=P, C_K=P,
+             C_V=P, C_dt=BF16, s_K=None, s_V=None, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return L.wsvd_append_latent(a["nb"], a["E"], a["nh"], a["r"], a["L_cap"], v(a["x"]), a["x_dt"], v(a["A_K"]),
+                                v(a["A_V"]), a["A_dt"], v(a["pos"]), v(a["C_K"]), v(a["C_V"]), a["C_dt"],
+                                v(a["s_K"]), v(a["s_V"]), v(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), ESHAPE), (dict(E=-4), ESHAPE), (dict(L_cap=0), ESHAPE),
+    (dict(x=None), ENULL), (dict(A_V=None), ENULL), (dict(pos=None), ENULL), (dict(C_K=None), ENULL),
+    (dict(x_dt=F32), EDTYPE), (dict(A_dt=F16), EDTYPE), (dict(C_dt=F16), EDTYPE),
+    (dict(C_dt=I8), EUNSUP), (dict(r=40), EUNSUP), (dict(E=4000), EUNSUP),
+    (dict(s_K=P), ESHAPE),
+    (dict(x=P + 2), EALIGN), (dict(A_K=P + 8), EALIGN), (dict(C_V=P + 4), EALIGN),
+    (dict(ws=None), EWS), (dict(ws_bytes=100), EWS),
+])
+def test_append_rejects(L, kw, want):
+    assert append(L, **kw) == want
+
+
+def test_binding_refuses_cpu_tensors(L):
+    q = torch.zeros(1, 4, 64)
+    c = torch.zeros(1, 4, 256, 16)
+    b = torch.zeros(4, 16, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        wsvd.decode_attn(q, c, c, b, b, torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max|gpu - ref| / max|ref| <= 1e-5 for the fp32 workload and <= 2e-2
+for bf16 / int8 workloads.  Small cases compare every output; the full-size
+workloads run in the launch configuration the benchmark times (automatic
+splits) and compare sampled (b, h) rows the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from rank_kv_cache_flash_amd import inputs as I
+from rank_kv_cache_flash_amd.configs import CONFIGS
+from tests.golden import make_golden as G
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2, "i8": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def W():
+    from rank_kv_cache_flash_amd import wsvd
+    wsvd.lib()
+    return wsvd
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0))
+
+
+def run_decode(W, inp, n_splits=None, out_dtype=None, softmax_scale=None, poison=False, partials_only=False):
+    d = W.device_inputs(inp)
+    ws = None
+    if poison:
+        nb, nh, H = inp.q.shape
+        need = W.decode_workspace_bytes(nb, nh, H, inp.L_cap, n_splits or 0)
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
+    out, o_part, lse = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], s_K=d.get("s_K"),
+                                     s_V=d.get("s_V"), n_splits=n_splits, out_dtype=out_dtype,
+                                     softmax_scale=softmax_scale, workspace=ws, partials_only=partials_only)
+    torch.cuda.synchronize()
+    return out, o_part, lse
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, gpu, ref, tol):
+    e = rel_err(gpu, ref)
+    print(f"[parity] {name}: max|err|/max|ref| = {e:.3e} (tol {tol:g})", flush=True)
+    assert np.all(np.isfinite(gpu)), name
+    assert e <= tol, f"{name}: {e} > {tol}"
+
+
+# ---------------------------------------------------------------------------
+# tiny fp32 workload (batch 1, 4 heads, H 64, r 16, L 256)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [None, 1, 2, 3, 7, 64, 256])
+def test_config1_fp32(W, S):
+    inp = CONFIGS[1].make()
+    out, _, _ = run_decode(W, inp, n_splits=S)
+    ref = O.decode_attn(inp)
+    check(f"config1 S={S}", f64(out), ref, TOL["f32"])
+    check(f"config1 S={S} vs stored", f64(out).reshape(-1), G.read("config1_out"), TOL["f32"])
+
+
+def test_config1_peaked_and_huge(W):
+    c = CONFIGS[1]
+    for gain in (4.0 * c.H, 300.0 * c.H):
+        inp = c.make(q_gain=gain)
+        out, _, _ = run_decode(W, inp)
+        check(f"config1 q_gain={gain}", f64(out), O.decode_attn(inp), TOL["f32"])
+    out, _, _ = run_decode(W, c.make(q_gain=4.0 * c.H))
+    check("config1 peaked vs stored", f64(out).reshape(-1), G.read("config1_peaked_out"), TOL["f32"])
+
+
+@pytest.mark.parametrize("S", [3, 7])
+def test_config1_partials_match_segments(W, S):
+    inp = CONFIGS[1].make(q_gain=2.0 * CONFIGS[1].H)
+    _, o_part, lse = run_decode(W, inp, n_splits=S, partials_only=True)
+    o_part, lse = f64(o_part), f64(lse)
+    for h in range(inp.nh):
+        ro, rl = O.decode_partials_one(inp, 0, h, S)
+        check(f"partials h={h} S={S}", o_part[0, h], ro, TOL["f32"])
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(lse[0, h]), fin)
+        assert np.max(np.abs(lse[0, h][fin] - rl[fin])) < 1e-5 * max(1.0, np.max(np.abs(rl[fin])))
+
+
+def test_config1_stored_partials(W):
+    inp = CONFIGS[1].make()
+    _, o_part, lse = run_decode(W, inp, n_splits=3, partials_only=True)
+    check("stored partials o", f64(o_part).reshape(-1), G.read("config1_split3_o"), TOL["f32"])
+    assert np.max(np.abs(f64(lse).reshape(-1) - G.read("config1_split3_lse"))) < 1e-5
+
+
+def test_combine_entry_point_matches_decode(W):
+    inp = CONFIGS[1].make()
+    out, _, _ = run_decode(W, inp, n_splits=5)
+    _, o_part, lse = run_decode(W, inp, n_splits=5, partials_only=True)
+    out2 = W.combine_splits(o_part.contiguous(), lse.contiguous(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_nan_poisoned_workspace_and_determinism(W):
+    inp = CONFIGS[1].make()
+    a, _, _ = run_decode(W, inp, n_splits=7, poison=True)
+    b, _, _ = run_decode(W, inp, n_splits=7)
+    assert torch.isfinite(a).all()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# small cases spanning several tiles, ragged tails, every (H, r, cache dtype)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,r", [(64, 16), (64, 32), (64, 48), (64, 64), (128, 16), (128, 32), (128, 48), (128, 64)])
+@pytest.mark.parametrize("C_dt", ["f32", "bf16", "i8"])
+def test_small_all_shapes(W, H, r, C_dt):
+    act = "f32" if C_dt == "f32" else "bf16"
+    L = np.array([300, 1, 0, 257, 129], np.int32)
+    inp = I.make_decode_inputs(5, 3, H, r, L, 300, seed=77 + H + r, act_dt=act, C_dt=C_dt,
+                               outlier_p=0.01 if C_dt == "i8" else 0.0, outlier_mul=20.0, q_gain=2.0 * H)
+    ref = O.decode_attn(inp)
+    for S in (None, 1, 3):
+        out, _, _ = run_decode(W, inp, n_splits=S)
+        g = f64(out)
+        check(f"H={H} r={r} C={C_dt} S={S}", g, ref, TOL[C_dt])
+        assert not g[2].any(), "L = 0 must give a zero row"
+
+
+def test_length_clamp_and_single_token(W):
+    L = np.array([1, 40, 4000], np.int32)   # last one exceeds L_cap = 64
+    inp = I.make_decode_inputs(3, 4, 128, 32, L, 64, seed=5, act_dt="bf16", C_dt="bf16", fill=np.minimum(L, 64))
+    out, _, _ = run_decode(W, inp, n_splits=4)
+    check("clamp/single", f64(out), O.decode_attn(inp), TOL["bf16"])
+
+
+def test_mixed_dtypes_and_scale(W):
+    inp = I.make_decode_inputs(2, 4, 128, 64, 333, 333, seed=8, act_dt="f16", C_dt="bf16")
+    inp.B_K = I.f32_to_bf16_bits(O.upcast(inp.B_K, "f16").astype(np.float32))
+    inp.B_V = I.f32_to_bf16_bits(O.upcast(inp.B_V, "f16").astype(np.float32))
+    inp.B_dt = "bf16"
+    out, _, _ = run_decode(W, inp, out_dtype=torch.float32, softmax_scale=0.3)
+    check("q f16 / B bf16 / out f32, sigma 0.3", f64(out), O.decode_attn(inp, softmax_scale=0.3), TOL["f16"])
+
+
+def test_int8_zero_rows(W):
+    inp = I.make_decode_inputs(2, 2, 128, 32, 100, 100, seed=4, act_dt="bf16", C_dt="i8")
+    inp.C_K[0, 1, 10:20] = 0
+    inp.s_K[0, 1, 10:20] = np.float16(0)
+    inp.C_V[1, 0, :50] = 0
+    inp.s_V[1, 0, :50] = np.float16(0)
+    out, _, _ = run_decode(W, inp, n_splits=3)
+    check("int8 zero rows", f64(out), O.decode_attn(inp), TOL["i8"])
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+def sampled_pairs(nb, nh, k, seed):
+    g = np.random.default_rng(seed)
+    pairs = {(0, 0), (nb - 1, nh - 1), (0, nh - 1), (nb - 1, 0)}
+    while len(pairs) < min(k, nb * nh):
+        pairs.add((int(g.integers(nb)), int(g.integers(nh))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_full_size_sampled(W, cid):
+    c = CONFIGS[cid]
+    inp = c.make()
+    print(f"[parity] config {cid}: {c.describe()}", flush=True)
+    out, _, _ = run_decode(W, inp)
+    g = f64(out)
+    pairs = sampled_pairs(c.nb, c.nh, 48, cid)
+    ref = O.decode_attn(inp, pairs=pairs)
+    got = np.stack([g[b, h] for b, h in pairs])
+    want = np.stack([ref[p] for p in pairs])
+    check(f"config {cid} sampled", got, want, TOL[c.C_dt])
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_full_size_peaked(W, cid):
+    c = CONFIGS[cid]
+    inp = c.make(q_gain=4.0 * c.H)
+    out, _, _ = run_decode(W, inp)
+    pairs = sampled_pairs(c.nb, c.nh, 16, 100 + cid)
+    ref = O.decode_attn(inp, pairs=pairs)
+    g = f64(out)
+    check(f"config {cid} peaked", np.stack([g[b, h] for b, h in pairs]), np.stack([ref[p] for p in pairs]),
+          TOL[c.C_dt])
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 1088])
+def test_config2_split_sweep(W, S):
+    c = CONFIGS[2]
+    inp = c.make(q_gain=4.0 * c.H)
+    out, _, _ = run_decode(W, inp, n_splits=S)
+    check(f"config 2 S={S}", f64(out), O.decode_attn(inp), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# append (x . A_Kh into the cache) + decode
+# ---------------------------------------------------------------------------
+def appended_row_ok(gpu_bits, exact, x, A, nh, r):
+    """|gpu - exact| <= half a bf16 ulp of the stored value plus the fp32
+    accumulation bound E * 2^-24 * sum_e |x_e A_e| of a length-E dot."""
+    xx = O.upcast(x, "bf16")
+    AA = O.upcast(A, "bf16")
+    E = xx.shape[1]
+    mag = np.abs(xx) @ np.abs(AA)                     # [nb, nh*r]
+    bound_acc = E * 2.0 ** -24 * mag.reshape(exact.shape)
+    g = O.upcast(gpu_bits, "bf16")
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(g))[1] - 9)
+    return np.abs(g - exact) <= half_ulp + bound_acc + 1e-30
+
+
+def _append_case(W, inp):
+    d = W.device_inputs(inp)
+    W.append_latent(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"])
+    torch.cuda.synchronize()
+    CK_ref, CV_ref, cK, cV = O.apply_append(inp)
+    gK = d["C_K"].view(torch.int16).cpu().numpy().view(np.uint16)
+    gV = d["C_V"].view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(inp.nb):
+        p = int(inp.pos[b])
+        okK = appended_row_ok(gK[b, :, p], cK[b], inp.x[b:b + 1], inp.A_K, inp.nh, inp.r)
+        okV = appended_row_ok(gV[b, :, p], cV[b], inp.x[b:b + 1], inp.A_V, inp.nh, inp.r)
+        assert okK.all() and okV.all(), f"appended latent row of sequence {b} outside the rounding bound"
+    # untouched rows stay untouched
+    mask = np.ones(gK.shape[:3], bool)
+    for b in range(inp.nb):
+        mask[b, :, int(inp.pos[b])] = False
+    assert np.array_equal(gK[mask], inp.C_K[mask]) and np.array_equal(gV[mask], inp.C_V[mask])
+    return d, CK_ref, CV_ref
+
+
+def test_append_small(W):
+    inp = I.make_ragged_step_inputs(5, 4, 128, 48, 512, 3, 40, 40, seed=21)
+    inp.pos[3] = 40        # out of range: skipped
+    inp.pos[4] = -1        # out of range: skipped
+    d = W.device_inputs(inp)
+    W.append_latent(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"])
+    torch.cuda.synchronize()
+    gK = d["C_K"].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(gK[3:], inp.C_K[3:])
+    inp.pos[3] = inp.L[3] - 1
+    inp.pos[4] = inp.L[4] - 1
+    _append_case(W, inp)
+
+
+@pytest.mark.parametrize("r", [16, 32, 64])
+def test_append_ranks(W, r):
+    inp = I.make_ragged_step_inputs(7, 8, 64, r, 768, 2, 30, 30, seed=30 + r)
+    _append_case(W, inp)
+
+
+def test_config5_full_step(W):
+    c = CONFIGS[5]
+    inp = c.make()
+    print(f"[parity] config 5: {c.describe()} sum L = {int(inp.L.sum())}", flush=True)
+    d, CK_ref, CV_ref = _append_case(W, inp)
+    out, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"])
+    torch.cuda.synchronize()
+    g = f64(out)
+    pairs = sampled_pairs(c.nb, c.nh, 48, 5)
+    ref = O.decode_attn(inp, C_K=CK_ref, C_V=CV_ref, pairs=pairs)
+    check("config 5 sampled", np.stack([g[b, h] for b, h in pairs]), np.stack([ref[p] for p in pairs]),
+          TOL["bf16"])
