@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Benchmark of the WSVD low-rank decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--also 3,4,5]
+
+A step is one pass of the whole hot path over one batch: (append of the new
+token's latents when the workload has one, then) the split decode and the
+split merge.  Inputs are resident in HBM before timing starts.  Steps are
+captured once into a HIP graph (rotating through enough copies of the
+inputs that every step reads cold HBM) and the graph is replayed; the K
+timed steps are bracketed by device synchronisation and timed with events
+on the replay stream.
+
+Prints ONE JSON line.  `value` is achieved GB/s = algorithmic bytes per step
+/ time per step (higher is better); `ms_per_step` gives the time.  The
+`roofline` object covers the dominant kernel (the split decode), timed live
+in its own graph of K back-to-back launches; `cpu_baseline` is the fp64
+oracle timed on the host on a bounded sample; `per_config` repeats the
+measurement on the other workloads with fewer steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused low-rank decode attn: µs/step and achieved HBM GB/s (% of peak), 1 GPU"
+COLD_BYTES = 1 << 30      # rotate input copies until >= 1 GiB is touched
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = ["decode.hip", "wsvd_common.hpp"]
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rank_kv_cache_flash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workload on the device
+# ---------------------------------------------------------------------------
+class Workload:
+    def __init__(self, cfg, copies=None, n_splits=None):
+        import torch
+        from rank_kv_cache_flash_amd import wsvd
+
+        self.cfg = cfg
+        t0 = time.time()
+        self.inp = cfg.make()
+        self.gen_s = time.time() - t0
+        self.L = self.inp.L.copy()
+        self.step_bytes = cfg.step_bytes(self.L)
+        self.decode_bytes = cfg.decode_bytes(self.L)
+        # bytes the split-decode kernel itself must read (out is written by the merge)
+        sa = {"f32": 4, "bf16": 2, "f16": 2}[cfg.act_dt]
+        self.decode_kernel_bytes = self.decode_bytes - cfg.nb * cfg.nh * cfg.H * sa
+        if copies is None:
+            copies = 1 if cfg.has_append else max(1, min(256, math.ceil(COLD_BYTES / self.decode_bytes)))
+        self.copies = copies
+        base = wsvd.device_inputs(self.inp)
+        nb, nh, H = self.inp.q.shape
+        self.sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+        need = wsvd.decode_workspace_bytes(nb, nh, H, cfg.L_cap, n_splits or 0)
+        self.ws = wsvd.decode_workspace(nb, nh, H, cfg.L_cap, n_splits or 0)       # counters start at zero
+        self.ws_dec = wsvd.decode_workspace(nb, nh, H, cfg.L_cap, n_splits or 0)
+        self.out = torch.empty((nb, nh, H), dtype=self.sets[0]["q"].dtype, device="cuda")
+        self.S = wsvd.decode_num_splits(nb, nh, cfg.L_cap, n_splits or 0)
+        self.full = []
+        self.dec_only = []
+        for d in self.sets:
+            kw = dict(s_K=d.get("s_K"), s_V=d.get("s_V"), n_splits=n_splits)
+            steps = []
+            if cfg.has_append:
+                aw = torch.empty(wsvd.append_workspace_bytes(nb, cfg.E, nh, cfg.r), dtype=torch.uint8,
+                                 device="cuda")
+                d["_aws"] = aw
+                steps.append(wsvd.PreparedAppend(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"],
+                                                 workspace=aw))
+            steps.append(wsvd.PreparedDecode(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"],
+                                             workspace=self.ws, out=self.out, **kw))
+            self.full.append(steps)
+            self.dec_only.append(wsvd.PreparedDecode(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"],
+                                                     workspace=self.ws_dec, out=None, **kw))
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        for call in self.full[i % self.copies]:
+            call()
+
+    def decode_only(self, i):
+        self.dec_only[i % self.copies]()
+
+
+def graph_time(fn, n, warmup_eager, repeats=1):
+    """Capture n calls of fn(i) in one graph; replay; return seconds per call
+    for each timed replay (first replay is untimed)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(warmup_eager):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e-3 / n)
+    del g
+    return out
+
+
+def eager_time(fn, n, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / n
+
+
+def load_traffic(workload_name, launches_bytes):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload_name)
+    if not rec or rec.get("kernel_src_sha256_16") != kernel_src_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host (bounded sample)
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, gpu_out, budget_s=12.0):
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle as O
+
+    cfg = w.cfg
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    with threadpool_limits(limits=ncpu):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        inp = w.inp
+        C_K, C_V = inp.C_K, inp.C_V
+        if cfg.has_append:
+            t0 = time.perf_counter()
+            C_K, C_V, _, _ = O.apply_append(inp)
+            t_append = time.perf_counter() - t0
+        else:
+            t_append = 0.0
+        # (b, h) pairs in a fixed order; run until the budget is spent
+        pairs = [(b, h) for b in range(cfg.nb) for h in range(cfg.nh)]
+        done = []
+        ref = {}
+        t0 = time.perf_counter()
+        k = 0
+        while True:
+            b, h = pairs[k % len(pairs)]
+            ref[(b, h)] = O.decode_attn_one(inp, b, h, C_K=C_K, C_V=C_V)
+            done.append((b, h))
+            k += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s and k >= min(len(pairs), 64):
+                break
+    # bytes the oracle consumed: the latents of the heads it did, factors once per head visited
+    sc = {"f32": 4, "bf16": 2, "i8": 1}[cfg.C_dt]
+    s_scale = 2 if cfg.C_dt == "i8" else 0
+    sa = {"f32": 4, "bf16": 2, "f16": 2}[cfg.act_dt]
+    lat = sum(int(w.L[b]) for b, _ in done) * 2 * (cfg.r * sc + s_scale)
+    per_head = 2 * cfg.r * cfg.H * sa + cfg.H * 2 * sa
+    nbytes = lat + per_head * len(done)
+    frac_of_step = len(done) / float(cfg.nb * cfg.nh)
+    step_s_equiv = (el + t_append) / frac_of_step if frac_of_step > 0 else float("nan")
+    # parity of this benchmark run against the oracle rows it computed
+    g = gpu_out.float().cpu().numpy().astype(np.float64)
+    got = np.stack([g[b, h] for b, h in ref])
+    want = np.stack([ref[p] for p in ref])
+    err = float(np.max(np.abs(got - want)) / np.max(np.abs(want)))
+    return {
+        "value": round(nbytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{len(done)} (sequence, head) rows of the {cfg.name} step in fp64, cycling over "
+                   f"the step's rows ({len(done) / (cfg.nb * cfg.nh):.3g} steps' worth; {el:.1f} s)"),
+        "us_per_step_equiv": round(step_s_equiv * 1e6, 1),
+        "host_cpus": ncpu,
+    }, err
+
+
+# ---------------------------------------------------------------------------
+def measure(cfg, steps, warmup, n_splits=None, repeats=3):
+    w = Workload(cfg, n_splits=n_splits)
+    t_step = graph_time(w.step, steps, warmup, repeats=repeats)
+    t_dec = graph_time(w.decode_only, steps, warmup, repeats=repeats)
+    return w, t_step, t_dec
+
+
+def summary(cfg, w, t_step, t_dec):
+    ts = t_step[0]
+    td = statistics.median(t_dec)
+    return {
+        "workload": cfg.name,
+        "shape": cfg.describe(),
+        "us_per_step": round(ts * 1e6, 3),
+        "us_per_step_replays": [round(t * 1e6, 3) for t in t_step],
+        "GB_per_s": round(w.step_bytes / ts / 1e9, 1),
+        "pct_of_hbm_peak": round(100.0 * w.step_bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
+        "step_bytes": int(w.step_bytes),
+        "decode_kernel_us": round(td * 1e6, 3),
+        "decode_kernel_GB_per_s": round(w.decode_kernel_bytes / td / 1e9, 1),
+        "splits": w.S,
+        "input_copies": w.copies,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--also", default="3,4,5", help="other workloads measured into per_config ('' for none)")
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--mode", choices=["bench", "decode-loop", "copy-calib"], default="bench",
+                    help="decode-loop / copy-calib: plain launch loops for counter collection")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    from rank_kv_cache_flash_amd import wsvd
+    from rank_kv_cache_flash_amd.configs import CONFIGS
+    wsvd.lib()
+
+    if args.mode == "copy-calib":
+        n = args.calib_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy-calib", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+        return
+    if args.mode == "decode-loop":
+        cfg = CONFIGS[args.config]
+        w = Workload(cfg, n_splits=args.splits or None)
+        for i in range(args.steps):
+            w.decode_only(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "decode-loop", "workload": cfg.name, "launches": args.steps,
+                          "decode_kernel_bytes": w.decode_kernel_bytes, "splits": w.S}))
+        return
+
+    cfg = CONFIGS[args.config]
+    w, t_step, t_dec = measure(cfg, args.steps, args.warmup, n_splits=args.splits or None)
+    main_sum = summary(cfg, w, t_step, t_dec)
+    ts = t_step[0]
+    td = statistics.median(t_dec)
+
+    achieved = w.decode_kernel_bytes / td / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(cfg.name, w.decode_kernel_bytes),
+                "kernel": "decode_split_kernel", "alg_bytes_per_launch": int(w.decode_kernel_bytes),
+                "avg_launch_us": round(td * 1e6, 3)}
+
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline(w, w.out, budget_s=args.cpu_budget)
+
+    per = {}
+    also = [int(x) for x in args.also.split(",") if x.strip()] if args.also else []
+    del w
+    torch.cuda.empty_cache()
+    for cid in also:
+        if cid == args.config:
+            continue
+        c = CONFIGS[cid]
+        k = max(10, min(args.steps, int(2e-2 / max(c.step_bytes() / 6e12, 1e-7))))
+        wc, tsc, tdc = measure(c, k, min(args.warmup, 10))
+        per[c.name] = summary(c, wc, tsc, tdc)
+        per[c.name]["steps"] = k
+        del wc
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": round(w_bytes_gbs(main_sum), 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ts * 1e3, 6),
+        "us_per_step": main_sum["us_per_step"],
+        "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_dt == "bf16" else cfg.act_dt,
+        "data": "synthetic (seeded N(0,1)/sqrt(dim) latents and factors; LLaVA-7B layer shapes)",
+        "config": {"workload": cfg.name, "shape": cfg.describe(), "splits": main_sum["splits"],
+                   "input_copies": main_sum["input_copies"], "timing": "hip-graph replay, cold HBM rotation"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_max_rel_err_vs_oracle": parity,
+        "per_config": per,
+        "kernel_src": kernel_src_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def w_bytes_gbs(s):
+    return s["GB_per_s"]
+
+
+if __name__ == "__main__":
+    main()

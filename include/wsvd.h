@@ -93,8 +93,14 @@ typedef enum wsvd_status {
  *                    wsvd_decode_num_splits).  Split s of a sequence with
  *                    l tokens covers [s*ceil(l/S), min(l, (s+1)*ceil(l/S))).
  *   workspace        device scratch of at least wsvd_decode_workspace_bytes
- *                    bytes, 256-byte aligned.  On return (stream order) it
- *                    holds the split partials:
+ *                    bytes, 256-byte aligned.  Its counter area (byte
+ *                    offset wsvd_decode_counter_offset(...), nb*nh uint32)
+ *                    must be zero before the first call that passes an
+ *                    output -- allocate the workspace zero-filled once;
+ *                    every call leaves the counters at zero again.  Calls
+ *                    in flight at the same time need separate workspaces.
+ *                    On return (stream order) the workspace holds the split
+ *                    partials:
  *                      o_part   float [nb, nh, S, H] at byte offset 0,
  *                               each split's attention normalised over its
  *                               own tokens (zeros for an empty split);
@@ -104,7 +110,10 @@ typedef enum wsvd_status {
  *                               (-inf for an empty split).
  *   out, out_dt      [nb, nh, H] F32 | BF16 | F16, or NULL to stop after the
  *                    partials (e.g. to merge partials from several devices
- *                    with wsvd_combine_splits).
+ *                    with wsvd_combine_splits).  With an output the whole
+ *                    step is one kernel launch: the last split of each
+ *                    (b, h) to finish merges that row's partials (in split
+ *                    order, so results do not depend on scheduling).
  *   stream           HIP stream to enqueue on (0 = null stream).
  */
 int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap,
@@ -181,6 +190,10 @@ size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_split
 
 /* Byte offset of lse_part inside the decode workspace.  Pure host. */
 size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits);
+
+/* Byte offset of the merge counters (nb*nh uint32) inside the decode
+ * workspace.  Pure host. */
+size_t wsvd_decode_counter_offset(int nb, int nh, int H, int L_cap, int n_splits);
 
 /* Workspace bytes wsvd_append_latent needs (0 on invalid sizes).  Pure host. */
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r);

@@ -12,8 +12,16 @@
 
 namespace {
 
-constexpr int kTargetBlocks = 2048;  // ~8 split blocks per CU on 256 CUs
-constexpr int kMinSplitTokens = 128; // below this a split's fixed cost dominates
+// Automatic split choice, tuned on MI355X (256 CUs).  Each split block pays a
+// fixed cost (both factors from L2, q' = B_K q, the projection and, with more
+// than one split, the merge), so splits are only added where they buy
+// parallelism: small batches get enough blocks to cover the CUs, large ones
+// keep whole sequences per block and only cut very long caches (which also
+// evens out ragged lengths).
+constexpr long kFillBlocks = 256;       // blocks wanted for a small batch
+constexpr int kMinSplitTokens = 256;    // never cut sequences finer than this
+constexpr int kLongTokens = 2048;       // per-split length cap for large batches
+constexpr long kLargeBatchPairs = 1024; // (b, h) pairs that make a batch "large"
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -28,9 +36,14 @@ int resolve_splits(int nb, int nh, int L_cap, int n_splits) {
     if (nb <= 0 || nh <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
     if (n_splits > 0) return n_splits > L_cap ? WSVD_ERR_SHAPE : n_splits;
     const long bh = (long)nb * nh;
-    long s = (kTargetBlocks + bh - 1) / bh;
-    const long smax = (L_cap + kMinSplitTokens - 1) / kMinSplitTokens;
-    if (s > smax) s = smax;
+    long s = 1;
+    if (bh < kFillBlocks) {
+        s = (kFillBlocks + bh - 1) / bh;
+        const long smax = (L_cap + kMinSplitTokens - 1) / kMinSplitTokens;
+        if (s > smax) s = smax;
+    } else if (bh >= kLargeBatchPairs) {
+        s = (L_cap + kLongTokens - 1) / kLongTokens;
+    }
     if (s < 1) s = 1;
     return (int)s;
 }
@@ -51,10 +64,16 @@ size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits) {
     return round_up(opart_bytes(nb, nh, H, S), 256);
 }
 
-size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_splits) {
+size_t wsvd_decode_counter_offset(int nb, int nh, int H, int L_cap, int n_splits) {
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0 || H <= 0) return 0;
     return round_up(opart_bytes(nb, nh, H, S), 256) + round_up((size_t)nb * nh * S * sizeof(float), 256);
+}
+
+size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_splits) {
+    const size_t off = wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits);
+    if (off == 0) return 0;
+    return off + round_up((size_t)nb * nh * sizeof(unsigned), 256);
 }
 
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r) {
@@ -119,13 +138,13 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, 
     a.scale_log2 = sigma * wsvd::kLog2e;
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
+    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                             wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits));
+    a.out = out;
+    a.out_dt = out ? (int)out_dt : 0;
 
-    if (wsvd::launch_decode_split(a, H, r, C_dt, stream) != hipSuccess) return WSVD_ERR_HIP;
-    if (out) {
-        if (wsvd::launch_combine(nb, nh, H, S, a.o_part, a.lse_part, out, out_dt, stream) != hipSuccess)
-            return WSVD_ERR_HIP;
-    }
-    return WSVD_OK;
+    // One launch: splits, and (with out) the merge by each head's last split.
+    return wsvd::launch_decode_split(a, H, r, C_dt, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
 int wsvd_combine_splits(int nb, int nh, int H, int n_splits, const float* o_part, const float* lse_part, void* out,

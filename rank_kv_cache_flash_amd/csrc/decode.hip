@@ -18,11 +18,23 @@
 // Hot-loop layout (gfx950, wave64).  A lane owns a 16-byte chunk of a latent
 // row: EPC = 16 / sizeof(element) consecutive dims.  G = r / EPC lanes hold
 // one row; rows sit in slots of GP = next_pow2(G) lanes (lanes j >= G of a
-// slot are idle and contribute zeros), so one wave-wide 16-byte load reads
-// RW = 64 / GP consecutive rows -- one contiguous block of HBM.  The score
-// of a row is reduced inside its slot with DPP row operations.  Each slot
-// keeps its own running max / sum (online softmax); slots, waves and then
-// splits are merged by log-sum-exp weights.
+// slot repeat chunk G-1 with a zero q' slice), so one wave-wide 16-byte load
+// reads RW = 64 / GP consecutive rows -- one contiguous block of HBM.  The
+// score of a row is reduced inside its slot with DPP row operations.  Each
+// slot keeps its own running max / sum (online softmax); slots, waves and
+// then splits are merged by log-sum-exp weights.  The loop has no divergent
+// branch: rows past the end of the split re-read the split's last row and
+// get a score of -inf.  Each wave double-buffers U row batches in registers,
+// so the next batches are in flight while the current ones are consumed.
+//
+// Prologue: q, both factors and the first latent batches are requested
+// before anything waits.  q' = B_K q is formed from the factor chunks held
+// in registers; B_V stays in LDS for the projection at the end.
+//
+// Merge: when an output is requested, each split stores its partial, then
+// the last split of a (b, h) to finish (a per-(b, h) counter in the
+// workspace, reset by that split) merges all of them in split order -- so
+// one launch does the whole step and the result is deterministic.
 //
 // int8 rows are converted with the byte-to-float instructions after an
 // xor with 0x80 (value = byte - 128); the -128 offset is folded into a
@@ -40,7 +52,30 @@ template <> struct CacheTraits<WSVD_I8> { static constexpr int EPC = 16; static 
 
 constexpr int next_pow2(int x) { return x <= 1 ? 1 : 2 * next_pow2((x + 1) / 2); }
 
-// Dot of one 16-byte chunk with the lane's slice of q'.
+// Element e of a 16-byte chunk of a factor of dtype BT, as float.
+template <int BT>
+__device__ __forceinline__ float chunk_elem(const u32x4& d, int e) {
+    if constexpr (BT == WSVD_F32) {
+        return __uint_as_float(d[e]);
+    } else if constexpr (BT == WSVD_BF16) {
+        return (e & 1) ? bf16_hi(d[e >> 1]) : bf16_lo(d[e >> 1]);
+    } else {
+        return f16_to_f32((e & 1) ? uint16_t(d[e >> 1] >> 16) : uint16_t(d[e >> 1] & 0xffffu));
+    }
+}
+
+template <int BT>
+__device__ __forceinline__ float raw_elem(const void* base, int idx) {
+    if constexpr (BT == WSVD_F32) {
+        return static_cast<const float*>(base)[idx];
+    } else if constexpr (BT == WSVD_BF16) {
+        return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+    } else {
+        return f16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+    }
+}
+
+// Dot of one 16-byte latent chunk with the lane's slice of q'.
 template <int CT>
 __device__ __forceinline__ float chunk_dot(const u32x4& d, const float* qp) {
     float acc = 0.f;
@@ -86,7 +121,19 @@ __device__ __forceinline__ void chunk_axpy(const u32x4& d, float w, float* acc) 
     }
 }
 
-template <int H, int R, int CT, int U>
+// q element as float from one unconditional dword load (dtype selected
+// arithmetically, no branch), so the prologue's loads stay straight-line.
+__device__ __forceinline__ float load_q_elem(const void* q, int q_dt, size_t idx) {
+    const bool wide = (q_dt == WSVD_F32);
+    const size_t word = wide ? idx : (idx >> 1);
+    const uint32_t w = static_cast<const uint32_t*>(q)[word];
+    const uint16_t half = (idx & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
+    const float fb = bf16_to_f32(half);
+    const float fh = f16_to_f32(half);
+    return wide ? __uint_as_float(w) : (q_dt == WSVD_BF16 ? fb : fh);
+}
+
+template <int H, int R, int CT, int BT, int U>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     using T = CacheTraits<CT>;
     constexpr int EPC = T::EPC;
@@ -98,13 +145,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     constexpr int NW = 4;
     constexpr int TILE = U * RW;
     constexpr bool I8 = (CT == WSVD_I8);
+    constexpr int BES = (BT == WSVD_F32) ? 4 : 2;  // factor element bytes
+    constexpr int BEPC = 16 / BES;                 // factor elements per chunk
+    constexpr int NBC = R * H / BEPC;              // chunks per factor
+    constexpr int NBT = (NBC + 255) / 256;         // chunks per thread
+    constexpr int CPR = H / BEPC;                  // chunks per factor row
+    constexpr int NPART = 256 / H;                 // projection: threads per output
+    static_assert(R % NPART == 0, "projection split");
 
     __shared__ float sh_q[H];
+    __shared__ float sh_qpart[NBC];
     __shared__ float sh_qp[R];
+    __shared__ u32x4 sh_bv[NBC];
     __shared__ float sh_red_o[NW][R];
     __shared__ float sh_red_m[NW];
     __shared__ float sh_red_l[NW];
     __shared__ float sh_on[R];
+    __shared__ float sh_proj[256];
+    __shared__ int sh_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -118,177 +176,296 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int rest = bid / a.nh;
     const int s = rest % a.S;
     const int b = rest / a.S;
+    const int S = a.S;
 
     int ell = a.L[b];
     ell = min(max(ell, 0), a.L_cap);
-    const int chunk = (ell + a.S - 1) / a.S;
+    const int chunk = (ell + S - 1) / S;
     const int t0 = min(ell, s * chunk);
     const int t1 = min(ell, t0 + chunk);
-
-    const size_t bh = (size_t)b * a.nh + h;
-    float* o_out = a.o_part + (bh * a.S + s) * H;
-    if (t0 >= t1) {  // empty split: uniform over the block
-        for (int i = tid; i < H; i += 256) o_out[i] = 0.f;
-        if (tid == 0) a.lse_part[bh * a.S + s] = kNegInf;
-        return;
-    }
-
-    // ---- prologue: q' = (sigma log2 e) B_K[h] q ---------------------------
-    for (int i = tid; i < H; i += 256) sh_q[i] = load_elem(a.q, a.q_dt, bh * H + i);
-    __syncthreads();
-    {
-        const int i = tid >> 2, qq = tid & 3;
-        float acc = 0.f;
-        if (i < R) {
-            const size_t base = ((size_t)h * R + i) * H + qq * (H / 4);
-#pragma unroll 8
-            for (int j = 0; j < H / 4; ++j) acc = fmaf(load_elem(a.B_K, a.B_dt, base + j), sh_q[qq * (H / 4) + j], acc);
-        }
-        acc = group_sum<4>(acc);
-        if (i < R && qq == 0) sh_qp[i] = acc * a.scale_log2;
-    }
-    __syncthreads();
-
-    const int g = lane / GP;
-    const int j = lane % GP;
-    const bool act = j < G;
-    float qp[EPC];
-#pragma unroll
-    for (int c = 0; c < EPC; ++c) qp[c] = act ? sh_qp[min(j, G - 1) * EPC + c] : 0.f;
-    float qoff = 0.f;  // int8: sum of the lane's q' slice, times 128
-    if constexpr (I8) {
-#pragma unroll
-        for (int c = 0; c < EPC; ++c) qoff += qp[c];
-        qoff *= 128.f;
-    }
-
-    // ---- hot loop ----------------------------------------------------------
-    const size_t row_bytes = (size_t)R * T::SZ;
-    const char* kbase = static_cast<const char*>(a.C_K) + (bh * a.L_cap + t0) * row_bytes + j * 16;
-    const char* vbase = static_cast<const char*>(a.C_V) + (bh * a.L_cap + t0) * row_bytes + j * 16;
-    const uint16_t* skb = I8 ? a.s_K + bh * a.L_cap + t0 : nullptr;
-    const uint16_t* svb = I8 ? a.s_V + bh * a.L_cap + t0 : nullptr;
     const int ntok = t1 - t0;
 
-    float m = kNegInf, l = 0.f, pw = 0.f;
-    float acc[EPC];
-#pragma unroll
-    for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
+    const size_t bh = (size_t)b * a.nh + h;
+    float* o_out = a.o_part + (bh * S + s) * H;
+    float lse_out = kNegInf;
 
-    for (int tb = wave * TILE; tb < ntok; tb += NW * TILE) {
-        u32x4 kr[U], vr[U];
-        float sk[U], sv[U];
+    if (ntok > 0) {  // uniform over the block
+        // ---- requests: q, B_K, B_V, first latent batches ----------------------
+        float qv = 0.f;
+        if (tid < H) qv = load_q_elem(a.q, a.q_dt, bh * H + tid);
+        const char* bk_base = static_cast<const char*>(a.B_K) + (size_t)h * R * H * BES;
+        const char* bv_base = static_cast<const char*>(a.B_V) + (size_t)h * R * H * BES;
+        u32x4 bk[NBT], bv[NBT];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = tb + u * RW + g;
-            const bool rv = row < ntok;
-            if (rv && act) {
+        for (int k = 0; k < NBT; ++k) {
+            const int c = tid + 256 * k;
+            if (NBC % 256 == 0 || c < NBC) {
+                bk[k] = *reinterpret_cast<const u32x4*>(bk_base + (size_t)c * 16);
+                bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
+            }
+        }
+
+        const int g = lane / GP;
+        const int j = lane % GP;
+        const bool act = j < G;
+        const size_t row_bytes = (size_t)R * T::SZ;
+        const char* kbase = static_cast<const char*>(a.C_K) + (bh * a.L_cap + t0) * row_bytes + min(j, G - 1) * 16;
+        const char* vbase = static_cast<const char*>(a.C_V) + (bh * a.L_cap + t0) * row_bytes + min(j, G - 1) * 16;
+        const uint16_t* skb = I8 ? a.s_K + bh * a.L_cap + t0 : nullptr;
+        const uint16_t* svb = I8 ? a.s_V + bh * a.L_cap + t0 : nullptr;
+
+        u32x4 kA[U], vA[U], kB[U], vB[U];
+        float skA[U], svA[U], skB[U], svB[U];
+
+        auto load_tile = [&](int tb, u32x4* kr, u32x4* vr, float* sk, float* sv) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = min(tb + u * RW + g, ntok - 1);
                 kr[u] = load16_stream(kbase + (size_t)row * row_bytes);
                 vr[u] = load16_stream(vbase + (size_t)row * row_bytes);
-            } else {
-                kr[u] = u32x4{0u, 0u, 0u, 0u};
-                vr[u] = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (I8) {
+                    sk[u] = f16_to_f32(skb[row]);
+                    sv[u] = f16_to_f32(svb[row]);
+                }
             }
-            if constexpr (I8) {
-                sk[u] = rv ? f16_to_f32(skb[row]) : 0.f;
-                sv[u] = rv ? f16_to_f32(svb[row]) : 0.f;
-            }
-        }
-        float sc[U];
-        float mloc = kNegInf;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float part = chunk_dot<CT>(kr[u], qp);
-            if constexpr (I8) part -= qoff;  // zero chunks (idle lane / past the end) cancel too
-            float d = group_sum<GP>(part);
-            if constexpr (I8) d *= sk[u];
-            sc[u] = (tb + u * RW + g) < ntok ? d : kNegInf;
-            mloc = fmaxf(mloc, sc[u]);
-        }
-        const float mn = fmaxf(m, mloc);
-        const float mu = (mn == kNegInf) ? 0.f : mn;
-        const float alpha = fast_exp2(m - mu);
-        l *= alpha;
-        if constexpr (I8) pw *= alpha;
-#pragma unroll
-        for (int c = 0; c < EPC; ++c) acc[c] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float p = fast_exp2(sc[u] - mu);
-            l += p;
-            float w = p;
-            if constexpr (I8) {
-                w *= sv[u];
-                pw += w;
-            }
-            chunk_axpy<CT>(vr[u], w, acc);
-        }
-        m = mn;
-    }
+        };
 
-    // ---- merge slots inside the wave ---------------------------------------
-    float Mw = m;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) Mw = fmaxf(Mw, shfl_xor_f(Mw, off));
-    const float f = (m == kNegInf) ? 0.f : fast_exp2(m - Mw);
-    l *= f;
-#pragma unroll
-    for (int c = 0; c < EPC; ++c) acc[c] *= f;
-    if constexpr (I8) {
-        pw *= f;
-#pragma unroll
-        for (int c = 0; c < EPC; ++c) acc[c] -= 128.f * pw;
-    }
-#pragma unroll
-    for (int off = GP; off < 64; off <<= 1) {
-        l += shfl_xor_f(l, off);
-#pragma unroll
-        for (int c = 0; c < EPC; ++c) acc[c] += shfl_xor_f(acc[c], off);
-    }
-    if (g == 0 && act) {
-#pragma unroll
-        for (int c = 0; c < EPC; ++c) sh_red_o[wave][j * EPC + c] = acc[c];
-    }
-    if (lane == 0) {
-        sh_red_m[wave] = Mw;
-        sh_red_l[wave] = l;
-    }
-    __syncthreads();
+        int tb = wave * TILE;
+        if (tb < ntok) load_tile(tb, kA, vA, skA, svA);
 
-    // ---- merge waves, normalise, project through B_V ------------------------
-    float M = sh_red_m[0];
+        // ---- q' = (sigma log2 e) B_K q from the chunks in registers ------------
+        if (tid < H) sh_q[tid] = qv;
+        __syncthreads();
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sh_red_m[w]);
-    float wt[NW];
-    float Lt = 0.f;
+        for (int k = 0; k < NBT; ++k) {
+            const int c = tid + 256 * k;
+            if (NBC % 256 == 0 || c < NBC) {
+                const int col = (c % CPR) * BEPC;
+                float p = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        wt[w] = (sh_red_m[w] == kNegInf) ? 0.f : fast_exp2(sh_red_m[w] - M);
-        Lt += sh_red_l[w] * wt[w];
+                for (int e = 0; e < BEPC; ++e) p = fmaf(chunk_elem<BT>(bk[k], e), sh_q[col + e], p);
+                sh_qpart[c] = p;
+                sh_bv[c] = bv[k];
+            }
+        }
+        __syncthreads();
+        if (tid < R) {
+            float p = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPR; ++c) p += sh_qpart[tid * CPR + c];
+            sh_qp[tid] = p * a.scale_log2;
+        }
+        __syncthreads();
+
+        float qp[EPC];
+#pragma unroll
+        for (int c = 0; c < EPC; ++c) qp[c] = act ? sh_qp[min(j, G - 1) * EPC + c] : 0.f;
+        float qoff = 0.f;  // int8: 128 * sum of the lane's q' slice
+        if constexpr (I8) {
+#pragma unroll
+            for (int c = 0; c < EPC; ++c) qoff += qp[c];
+            qoff *= 128.f;
+        }
+
+        // ---- hot loop ----------------------------------------------------------
+        float m = kNegInf, l = 0.f, pw = 0.f;
+        float acc[EPC];
+#pragma unroll
+        for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
+
+        auto consume = [&](int tbc, const u32x4* kr, const u32x4* vr, const float* sk, const float* sv) {
+            float sc[U];
+            float mloc = kNegInf;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float part = chunk_dot<CT>(kr[u], qp);
+                if constexpr (I8) part -= qoff;
+                float d = group_sum<GP>(part);
+                if constexpr (I8) d *= sk[u];
+                sc[u] = (tbc + u * RW + g) < ntok ? d : kNegInf;
+                mloc = fmaxf(mloc, sc[u]);
+            }
+            const float mn = fmaxf(m, mloc);
+            const float mu = (mn == kNegInf) ? 0.f : mn;
+            const float alpha = fast_exp2(m - mu);
+            l *= alpha;
+            if constexpr (I8) pw *= alpha;
+#pragma unroll
+            for (int c = 0; c < EPC; ++c) acc[c] *= alpha;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = fast_exp2(sc[u] - mu);
+                l += p;
+                float w = p;
+                if constexpr (I8) {
+                    w *= sv[u];
+                    pw += w;
+                }
+                chunk_axpy<CT>(vr[u], w, acc);
+            }
+            m = mn;
+        };
+
+        while (tb < ntok) {
+            int tn = tb + NW * TILE;
+            if (tn < ntok) load_tile(tn, kB, vB, skB, svB);
+            consume(tb, kA, vA, skA, svA);
+            tb = tn;
+            if (tb >= ntok) break;
+            tn = tb + NW * TILE;
+            if (tn < ntok) load_tile(tn, kA, vA, skA, svA);
+            consume(tb, kB, vB, skB, svB);
+            tb = tn;
+        }
+
+        // ---- merge slots inside the wave ---------------------------------------
+        float Mw = m;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) Mw = fmaxf(Mw, shfl_xor_f(Mw, off));
+        const float f = (m == kNegInf) ? 0.f : fast_exp2(m - Mw);
+        l *= f;
+#pragma unroll
+        for (int c = 0; c < EPC; ++c) acc[c] *= f;
+        if constexpr (I8) {
+            pw *= f;
+#pragma unroll
+            for (int c = 0; c < EPC; ++c) acc[c] -= 128.f * pw;
+        }
+#pragma unroll
+        for (int off = GP; off < 64; off <<= 1) {
+            l += shfl_xor_f(l, off);
+#pragma unroll
+            for (int c = 0; c < EPC; ++c) acc[c] += shfl_xor_f(acc[c], off);
+        }
+        if (g == 0 && act) {
+#pragma unroll
+            for (int c = 0; c < EPC; ++c) sh_red_o[wave][j * EPC + c] = acc[c];
+        }
+        if (lane == 0) {
+            sh_red_m[wave] = Mw;
+            sh_red_l[wave] = l;
+        }
+        __syncthreads();
+
+        // ---- merge waves, normalise, project through B_V ------------------------
+        float M = sh_red_m[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sh_red_m[w]);
+        float wt[NW];
+        float Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            wt[w] = (sh_red_m[w] == kNegInf) ? 0.f : fast_exp2(sh_red_m[w] - M);
+            Lt += sh_red_l[w] * wt[w];
+        }
+        if (tid < R) {
+            float o = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) o = fmaf(sh_red_o[w][tid], wt[w], o);
+            sh_on[tid] = o / Lt;
+        }
+        __syncthreads();
+        {
+            const int jj = tid % H;
+            const int part = tid / H;
+            constexpr int RP = R / NPART;
+            const void* bvr = static_cast<const void*>(sh_bv);
+            float o = 0.f;
+#pragma unroll
+            for (int i = part * RP; i < (part + 1) * RP; ++i) o = fmaf(sh_on[i], raw_elem<BT>(bvr, i * H + jj), o);
+            sh_proj[tid] = o;
+        }
+        __syncthreads();
+        if (tid < H) {
+            float o = 0.f;
+#pragma unroll
+            for (int p = 0; p < NPART; ++p) o += sh_proj[p * H + tid];
+            store_coherent(o_out + tid, o);
+            if (S == 1 && a.out) store_elem(a.out, a.out_dt, bh * H + tid, o);
+        }
+        lse_out = (M + fast_log2(Lt)) * kLn2;
+    } else {
+        for (int i = tid; i < H; i += 256) {
+            store_coherent(o_out + i, 0.f);
+            if (S == 1 && a.out) store_elem(a.out, a.out_dt, bh * H + i, 0.f);
+        }
     }
-    if (tid < R) {
-        float o = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) o = fmaf(sh_red_o[w][tid], wt[w], o);
-        sh_on[tid] = o / Lt;
-    }
+    if (tid == 0) store_coherent(a.lse_part + bh * S + s, lse_out);
+
+    // ---- last split of (b, h) merges all partials ------------------------------
+    // The partials were stored write-through at device scope; once every wave
+    // has seen its stores complete, one relaxed device-scope increment
+    // publishes them.  The split that brings the count to S reads them back
+    // with device-scope loads (not served from a stale L2 line), so no
+    // cache-wide writeback or invalidate is needed.
+    if (!a.out || S == 1) return;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int jj = tid; jj < H; jj += 256) {
-        float o = 0.f;
-        const size_t base = (size_t)h * R * H + jj;
-#pragma unroll 8
-        for (int i = 0; i < R; ++i) o = fmaf(sh_on[i], load_elem(a.B_V, a.B_dt, base + (size_t)i * H), o);
-        o_out[jj] = o;
+    if (tid == 0)
+        sh_last = (__hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned)(S - 1));
+    __syncthreads();
+    if (!sh_last) return;
+    // Online merge over chunks of up to 256 splits: one parallel load of the
+    // chunk's lse values into LDS, then each output lane issues its o_part
+    // loads eight at a time before consuming them.
+    const float* lsp = a.lse_part + bh * S;
+    const float* opp = a.o_part + bh * S * H;
+    float Mrun = kNegInf, accm = 0.f, wsum = 0.f;
+    for (int k0 = 0; k0 < S; k0 += 256) {
+        const int n = min(256, S - k0);
+        __syncthreads();
+        if (tid < n) sh_proj[tid] = load_coherent(lsp + k0 + tid);
+        __syncthreads();
+        float cm = kNegInf;
+        for (int k = 0; k < n; ++k) cm = fmaxf(cm, sh_proj[k]);
+        const float Mn = fmaxf(Mrun, cm);
+        if (Mn == kNegInf) continue;
+        const float rs = (Mrun == kNegInf) ? 0.f : fast_exp2((Mrun - Mn) * kLog2e);
+        accm *= rs;
+        wsum *= rs;
+        Mrun = Mn;
+        if (tid < H) {
+            for (int k = 0; k < n; k += 8) {
+                float ov[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    ov[u] = (k + u < n) ? load_coherent(opp + (size_t)(k0 + k + u) * H + tid) : 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (k + u < n) {
+                        const float lv = sh_proj[k + u];
+                        const float w = (lv == kNegInf) ? 0.f : fast_exp2((lv - Mn) * kLog2e);
+                        wsum += w;
+                        accm = fmaf(w, ov[u], accm);
+                    }
+                }
+            }
+        }
     }
-    if (tid == 0) a.lse_part[bh * a.S + s] = (M + fast_log2(Lt)) * kLn2;
+    if (tid < H) store_elem(a.out, a.out_dt, bh * H + tid, wsum > 0.f ? accm / wsum : 0.f);
+    if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int H, int R, int CT, int BT>
+static hipError_t launch_hrcb(const DecodeArgs& a, hipStream_t st) {
+    // Row batches per buffer: int8 chunks carry 16 codes per lane, so two
+    // batches (double-buffered) keep the kernel under 128 VGPRs -- four
+    // blocks per CU.
+    constexpr int U = (CT == WSVD_I8) ? 2 : 4;
+    const unsigned nblk = (unsigned)((size_t)a.nb * a.nh * a.S);
+    hipLaunchKernelGGL((decode_split_kernel<H, R, CT, BT, U>), dim3(nblk), dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 template <int H, int R, int CT>
 static hipError_t launch_hrc(const DecodeArgs& a, hipStream_t st) {
-    constexpr int U = 4;
-    const unsigned nblk = (unsigned)((size_t)a.nb * a.nh * a.S);
-    hipLaunchKernelGGL((decode_split_kernel<H, R, CT, U>), dim3(nblk), dim3(256), 0, st, a);
-    return hipGetLastError();
+    switch (a.B_dt) {
+        case WSVD_F32: return launch_hrcb<H, R, CT, WSVD_F32>(a, st);
+        case WSVD_BF16: return launch_hrcb<H, R, CT, WSVD_BF16>(a, st);
+        case WSVD_F16: return launch_hrcb<H, R, CT, WSVD_F16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int H, int R>

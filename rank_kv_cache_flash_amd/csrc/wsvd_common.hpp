@@ -85,6 +85,16 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Device-scope (all XCDs) coherent store / load: written through to memory,
+// read past any L2 copy, so partials written by one XCD can be merged on
+// another without a cache-wide writeback or invalidate.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte global load marked non-temporal: the latent stream is read once,

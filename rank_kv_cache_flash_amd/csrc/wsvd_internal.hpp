@@ -24,6 +24,9 @@ struct DecodeArgs {
     float scale_log2;  // softmax scale times log2(e)
     float* o_part;     // [nb, nh, S, H]
     float* lse_part;   // [nb, nh, S]
+    unsigned* counters;  // [nb, nh] arrival counters (zero between calls)
+    void* out;         // [nb, nh, H] or null (partials only)
+    int out_dt;
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipStream_t st);

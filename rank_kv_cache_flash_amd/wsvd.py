@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.wsvd_decode_workspace_bytes.restype = sz
     L.wsvd_decode_lse_offset.argtypes = [i32, i32, i32, i32, i32]
     L.wsvd_decode_lse_offset.restype = sz
+    L.wsvd_decode_counter_offset.argtypes = [i32, i32, i32, i32, i32]
+    L.wsvd_decode_counter_offset.restype = sz
     L.wsvd_append_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.wsvd_append_workspace_bytes.restype = sz
     L.wsvd_status_string.argtypes = [i32]
@@ -78,6 +80,15 @@ def decode_workspace_bytes(nb, nh, H, L_cap, n_splits=0) -> int:
 
 def decode_lse_offset(nb, nh, H, L_cap, n_splits=0) -> int:
     return int(lib().wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits or 0))
+
+
+def decode_counter_offset(nb, nh, H, L_cap, n_splits=0) -> int:
+    return int(lib().wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits or 0))
+
+
+def decode_workspace(nb, nh, H, L_cap, n_splits=0, device="cuda"):
+    """A decode workspace, zero-filled once (its merge counters must start at zero)."""
+    return torch.zeros(decode_workspace_bytes(nb, nh, H, L_cap, n_splits), dtype=torch.uint8, device=device)
 
 
 def append_workspace_bytes(nb, E, nh, r) -> int:
@@ -126,7 +137,7 @@ def decode_attn(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=N
         raise WsvdError(S, "wsvd_decode_num_splits")
     need = decode_workspace_bytes(nb, nh, H, L_cap, n_splits or 0)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(nb, nh, H, L_cap, n_splits or 0, device=q.device)
     if not partials_only and out is None:
         out = torch.empty((nb, nh, H), dtype=out_dtype or q.dtype, device=q.device)
     if partials_only:
@@ -218,3 +229,52 @@ def device_inputs(inp, device="cuda"):
         d["A_V"] = to_device(inp.A_V, inp.A_dt, device)
         d["pos"] = to_device(inp.pos, "i32", device)
     return d
+
+
+# ---------------------------------------------------------------------------
+# prepared calls: the ctypes argument tuple is built once, so issuing a step
+# costs one foreign call (used for launch-rate-sensitive timing and graphs)
+# ---------------------------------------------------------------------------
+class PreparedDecode:
+    """wsvd_decode_attn with fixed buffers; __call__(stream) enqueues it."""
+
+    def __init__(self, q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, workspace, out=None,
+                 softmax_scale=None, n_splits=None):
+        for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"),
+                     (s_K, "s_K"), (s_V, "s_V"), (out, "out"), (workspace, "workspace")):
+            _dev(t, n)
+        nb, nh, H = q.shape
+        L_cap, r = C_K.shape[2], C_K.shape[3]
+        self.S = decode_num_splits(nb, nh, L_cap, n_splits or 0)
+        self._keep = (q, C_K, C_V, B_K, B_V, L, s_K, s_V, workspace, out)
+        if s_K is not None and s_K.dtype == torch.float16:
+            s_K = s_K.view(torch.int16)
+        if s_V is not None and s_V.dtype == torch.float16:
+            s_V = s_V.view(torch.int16)
+        self._args = (nb, nh, H, r, L_cap, _ptr(L), _ptr(q), _DT[q.dtype], _ptr(C_K), _ptr(C_V), _DT[C_K.dtype],
+                      _ptr(s_K), _ptr(s_V), _ptr(B_K), _ptr(B_V), _DT[B_K.dtype], float(softmax_scale or 0.0),
+                      int(n_splits or 0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                      _ptr(out), _DT[out.dtype] if out is not None else 0)
+        self._fn = lib().wsvd_decode_attn
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)), "wsvd_decode_attn")
+
+
+class PreparedAppend:
+    """wsvd_append_latent with fixed buffers; __call__(stream) enqueues it."""
+
+    def __init__(self, x, A_K, A_V, pos, C_K, C_V, *, workspace):
+        for t, n in ((x, "x"), (A_K, "A_K"), (A_V, "A_V"), (pos, "pos"), (C_K, "C_K"), (C_V, "C_V"),
+                     (workspace, "workspace")):
+            _dev(t, n)
+        nb, E = x.shape
+        _, nh, L_cap, r = C_K.shape
+        self._keep = (x, A_K, A_V, pos, C_K, C_V, workspace)
+        self._args = (nb, E, nh, r, L_cap, _ptr(x), _DT[x.dtype], _ptr(A_K), _ptr(A_V), _DT[A_K.dtype], _ptr(pos),
+                      _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], None, None, _ptr(workspace),
+                      workspace.numel() * workspace.element_size())
+        self._fn = lib().wsvd_append_latent
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)), "wsvd_append_latent")

@@ -42,6 +42,7 @@ def run_decode(W, inp, n_splits=None, out_dtype=None, softmax_scale=None, poison
         nb, nh, H = inp.q.shape
         need = W.decode_workspace_bytes(nb, nh, H, inp.L_cap, n_splits or 0)
         ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
+        ws[W.decode_counter_offset(nb, nh, H, inp.L_cap, n_splits or 0):] = 0  # counters start at zero
     out, o_part, lse = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], s_K=d.get("s_K"),
                                      s_V=d.get("s_V"), n_splits=n_splits, out_dtype=out_dtype,
                                      softmax_scale=softmax_scale, workspace=ws, partials_only=partials_only)
@@ -117,6 +118,25 @@ def test_nan_poisoned_workspace_and_determinism(W):
     b, _, _ = run_decode(W, inp, n_splits=7)
     assert torch.isfinite(a).all()
     assert torch.equal(a, b)
+
+
+def test_merge_counters_reset_and_reuse(W):
+    """One workspace reused across calls and shapes: the counters come back to zero."""
+    inp = CONFIGS[2].make(q_gain=4.0 * CONFIGS[2].H)
+    d = W.device_inputs(inp)
+    nb, nh, H = inp.q.shape
+    ws = W.decode_workspace(nb, nh, H, inp.L_cap, 0)
+    off = W.decode_counter_offset(nb, nh, H, inp.L_cap, 0)
+    ref = O.decode_attn(inp)
+    outs = []
+    for _ in range(5):
+        out, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not ws[off:].any(), "merge counters must be zero after every call"
+    for o in outs:
+        assert torch.equal(o, outs[0])
+    check("config 2 reused workspace", f64(outs[0]), ref, TOL["bf16"])
 
 
 # ---------------------------------------------------------------------------
@@ -276,3 +296,24 @@ def test_config5_full_step(W):
     ref = O.decode_attn(inp, C_K=CK_ref, C_V=CV_ref, pairs=pairs)
     check("config 5 sampled", np.stack([g[b, h] for b, h in pairs]), np.stack([ref[p] for p in pairs]),
           TOL["bf16"])
+
+
+def test_merge_across_xcds_repeated(W):
+    """Many splits of one (b, h) land on every XCD (3 heads, so blocks of a
+    head do not share an XCD); the in-kernel merge must equal the separate
+    merge entry point bit for bit on every call."""
+    inp = I.make_decode_inputs(2, 3, 128, 32, 2000, 2000, seed=99, act_dt="bf16", C_dt="bf16", q_gain=300.0)
+    d = W.device_inputs(inp)
+    ws = W.decode_workspace(2, 3, 128, 2000, 64)
+    _, o_part, lse = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], n_splits=64,
+                                   partials_only=True, workspace=ws)
+    ref = W.combine_splits(o_part.clone(), lse.clone(), out_dtype=torch.bfloat16)
+    outs = []
+    for _ in range(20):
+        out, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], n_splits=64,
+                                  workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+    check("merge across XCDs", f64(ref), O.decode_attn(inp), TOL["bf16"])
