@@ -262,8 +262,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--mode", choices=["bench", "decode-loop", "copy-calib"], default="bench",
-                    help="decode-loop / copy-calib: plain launch loops for counter collection")
+    ap.add_argument("--mode", choices=["bench", "decode-loop", "copy-calib", "counters"], default="bench",
+                    help="decode-loop / copy-calib / counters: plain launch loops for counter collection")
+    ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
 
@@ -290,6 +291,30 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy-calib", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+        return
+    if args.mode == "counters":
+        # 1) a plain device copy of known size (calibrates FETCH_SIZE / WRITE_SIZE),
+        # 2) for each workload, the split kernel alone on the benchmark's buffers.
+        n = args.calib_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        rec = {"copy_bytes": n * 4, "workloads": {}}
+        for cid in [int(x) for x in args.configs.split(",") if x.strip()]:
+            cfg = CONFIGS[cid]
+            w = Workload(cfg)
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                w.decode_only(i)
+            torch.cuda.synchronize()
+            rec["workloads"][cfg.name] = {"grid_blocks": w.cfg.nb * w.cfg.nh * w.S, "launches": args.steps,
+                                          "alg_bytes_per_launch": int(w.decode_kernel_bytes), "splits": w.S}
+            del w
+            torch.cuda.empty_cache()
+        print(json.dumps(rec))
         return
     if args.mode == "decode-loop":
         cfg = CONFIGS[args.config]
