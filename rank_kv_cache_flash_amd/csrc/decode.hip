@@ -22,14 +22,19 @@
 // reads RW = 64 / GP consecutive rows -- one contiguous block of HBM.  The
 // score of a row is reduced inside its slot with DPP row operations.  Each
 // slot keeps its own running max / sum (online softmax); slots, waves and
-// then splits are merged by log-sum-exp weights.  The loop has no divergent
-// branch: rows past the end of the split re-read the split's last row and
-// get a score of -inf.  Each wave double-buffers U row batches in registers,
-// so the next batches are in flight while the current ones are consumed.
+// then splits are merged by log-sum-exp weights.  Each wave double-buffers U
+// row batches in registers (tiles), so the next tile is in flight while the
+// current one is consumed.  The steady-state loop has no branch around a
+// load (rows past the end of the split re-read its last row and score
+// -inf), its buffers stay in fixed registers, and the tail requests only
+// tiles that exist.  Loads use a wave-uniform 64-bit base plus a 32-bit lane
+// offset (the scalar-base load form).
 //
-// Prologue: q, both factors and the first latent batches are requested
-// before anything waits.  q' = B_K q is formed from the factor chunks held
-// in registers; B_V stays in LDS for the projection at the end.
+// Prologue: q, both factors and the first latent tiles are requested before
+// anything waits.  q' = B_K q is formed from the factor chunks held in
+// registers; B_V stays in LDS for the projection at the end.  The in-wave
+// merge uses VALU cross-lane operations (DPP row rotations and the gfx950
+// permlane16/32 swaps), not LDS round trips.
 //
 // Merge: when an output is requested, each split stores its partial, then
 // the last split of a (b, h) to finish (a per-(b, h) counter in the
@@ -166,7 +171,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // Wave index through readfirstlane: the compiler then treats it (and the
+    // token loop bounds derived from it) as wave-uniform scalar values.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // Block -> (b, s, h) with h fastest: consecutive blocks land on different
     // XCDs round-robin, so with nh a multiple of 8 each head always runs on
@@ -208,30 +215,36 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const int g = lane / GP;
         const int j = lane % GP;
         const bool act = j < G;
-        const size_t row_bytes = (size_t)R * T::SZ;
-        const char* kbase = static_cast<const char*>(a.C_K) + (bh * a.L_cap + t0) * row_bytes + min(j, G - 1) * 16;
-        const char* vbase = static_cast<const char*>(a.C_V) + (bh * a.L_cap + t0) * row_bytes + min(j, G - 1) * 16;
-        const uint16_t* skb = I8 ? a.s_K + bh * a.L_cap + t0 : nullptr;
-        const uint16_t* svb = I8 ? a.s_V + bh * a.L_cap + t0 : nullptr;
+        constexpr uint32_t row_bytes = (uint32_t)R * T::SZ;
+        const char* kbase = static_cast<const char*>(a.C_K) + (bh * a.L_cap + t0) * row_bytes;
+        const char* vbase = static_cast<const char*>(a.C_V) + (bh * a.L_cap + t0) * row_bytes;
+        const char* skb = I8 ? reinterpret_cast<const char*>(a.s_K + bh * a.L_cap + t0) : nullptr;
+        const char* svb = I8 ? reinterpret_cast<const char*>(a.s_V + bh * a.L_cap + t0) : nullptr;
+        const uint32_t lane_off = (uint32_t)min(j, G - 1) * 16u;
 
         u32x4 kA[U], vA[U], kB[U], vB[U];
-        float skA[U], svA[U], skB[U], svB[U];
+        uint16_t skA[U], svA[U], skB[U], svB[U];
 
-        auto load_tile = [&](int tb, u32x4* kr, u32x4* vr, float* sk, float* sv) {
+        auto load_tile = [&](int tb, u32x4* kr, u32x4* vr, uint16_t* sk, uint16_t* sv) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int row = min(tb + u * RW + g, ntok - 1);
-                kr[u] = load16_stream(kbase + (size_t)row * row_bytes);
-                vr[u] = load16_stream(vbase + (size_t)row * row_bytes);
-                if constexpr (I8) {
-                    sk[u] = f16_to_f32(skb[row]);
-                    sv[u] = f16_to_f32(svb[row]);
+                const uint32_t row = (uint32_t)min(tb + u * RW + g, ntok - 1);
+                const uint32_t off = row * row_bytes + lane_off;
+                kr[u] = load16_stream(kbase + off);
+                vr[u] = load16_stream(vbase + off);
+                if constexpr (I8) {  // raw fp16 bits: converted when consumed, so no wait here
+                    sk[u] = *reinterpret_cast<const uint16_t*>(skb + row * 2u);
+                    sv[u] = *reinterpret_cast<const uint16_t*>(svb + row * 2u);
                 }
             }
         };
 
+        // This wave's tiles start at tb + k * STEP; the first two are requested
+        // before the prologue waits for anything.
+        constexpr int STEP = NW * TILE;
         int tb = wave * TILE;
         if (tb < ntok) load_tile(tb, kA, vA, skA, svA);
+        if (tb + STEP < ntok) load_tile(tb + STEP, kB, vB, skB, svB);
 
         // ---- q' = (sigma log2 e) B_K q from the chunks in registers ------------
         if (tid < H) sh_q[tid] = qv;
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
 
-        auto consume = [&](int tbc, const u32x4* kr, const u32x4* vr, const float* sk, const float* sv) {
+        auto consume = [&](int tbc, const u32x4* kr, const u32x4* vr, const uint16_t* sk, const uint16_t* sv) {
             float sc[U];
             float mloc = kNegInf;
 #pragma unroll
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 float part = chunk_dot<CT>(kr[u], qp);
                 if constexpr (I8) part -= qoff;
                 float d = group_sum<GP>(part);
-                if constexpr (I8) d *= sk[u];
+                if constexpr (I8) d *= f16_to_f32(sk[u]);
                 sc[u] = (tbc + u * RW + g) < ntok ? d : kNegInf;
                 mloc = fmaxf(mloc, sc[u]);
             }
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 l += p;
                 float w = p;
                 if constexpr (I8) {
-                    w *= sv[u];
+                    w *= f16_to_f32(sv[u]);
                     pw += w;
                 }
                 chunk_axpy<CT>(vr[u], w, acc);
@@ -306,22 +319,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             m = mn;
         };
 
-        while (tb < ntok) {
-            int tn = tb + NW * TILE;
-            if (tn < ntok) load_tile(tn, kB, vB, skB, svB);
-            consume(tb, kA, vA, skA, svA);
-            tb = tn;
-            if (tb >= ntok) break;
-            tn = tb + NW * TILE;
-            if (tn < ntok) load_tile(tn, kA, vA, skA, svA);
-            consume(tb, kB, vB, skB, svB);
-            tb = tn;
+        // Even tiles live in buffer A, odd tiles in B.  The steady-state loop
+        // consumes a pair and requests the next pair unconditionally; the tail
+        // requests only tiles that exist, so nothing is left in flight.
+        const int nt = (ntok > tb) ? (ntok - tb + STEP - 1) / STEP : 0;
+        int k = 0;
+        for (; k + 3 < nt; k += 2) {
+            consume(tb + k * STEP, kA, vA, skA, svA);
+            load_tile(tb + (k + 2) * STEP, kA, vA, skA, svA);
+            consume(tb + (k + 1) * STEP, kB, vB, skB, svB);
+            load_tile(tb + (k + 3) * STEP, kB, vB, skB, svB);
         }
+        const int rem = nt - k;
+        if (rem >= 1) consume(tb + k * STEP, kA, vA, skA, svA);
+        if (rem >= 3) load_tile(tb + (k + 2) * STEP, kA, vA, skA, svA);
+        if (rem >= 2) consume(tb + (k + 1) * STEP, kB, vB, skB, svB);
+        if (rem >= 3) consume(tb + (k + 2) * STEP, kA, vA, skA, svA);
 
-        // ---- merge slots inside the wave ---------------------------------------
-        float Mw = m;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) Mw = fmaxf(Mw, shfl_xor_f(Mw, off));
+        // ---- merge slots inside the wave (VALU cross-lane operations) ----------
+        const float Mw = wave_max(m);
         const float f = (m == kNegInf) ? 0.f : fast_exp2(m - Mw);
         l *= f;
 #pragma unroll
@@ -331,12 +347,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < EPC; ++c) acc[c] -= 128.f * pw;
         }
+        l = sum_over_slots<GP>(l);
 #pragma unroll
-        for (int off = GP; off < 64; off <<= 1) {
-            l += shfl_xor_f(l, off);
-#pragma unroll
-            for (int c = 0; c < EPC; ++c) acc[c] += shfl_xor_f(acc[c], off);
-        }
+        for (int c = 0; c < EPC; ++c) acc[c] = sum_over_slots<GP>(acc[c]);
         if (g == 0 && act) {
 #pragma unroll
             for (int c = 0; c < EPC; ++c) sh_red_o[wave][j * EPC + c] = acc[c];

@@ -64,7 +64,7 @@ constexpr int kDppRowMirror = 0x140;   // lane j of 16 <-> 15-j
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of a
@@ -76,6 +76,47 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
     if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
     return v;
+}
+
+// Lane l combined with lane l^16 (l^32): gfx950 permlane swaps exchange rows
+// of two registers; with both operands equal, the two results hold v_l and
+// v_(l^16) (v_(l^32)) in every lane.  VALU only, no LDS round trip.
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Maximum over the whole wave, in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return xor32_max(xor16_max(v));
+}
+
+// Sum over the lanes that share (lane % GP) -- one lane of every row slot of
+// GP lanes -- in every lane: rotations by GP, 2GP, .. inside each 16-lane
+// row (DPP row_ror), then across rows.
+template <int GP>
+__device__ __forceinline__ float sum_over_slots(float v) {
+    if constexpr (GP <= 1) v += dpp_f<0x121>(v);
+    if constexpr (GP <= 2) v += dpp_f<0x122>(v);
+    if constexpr (GP <= 4) v += dpp_f<0x124>(v);
+    if constexpr (GP <= 8) v += dpp_f<0x128>(v);
+    return xor32_sum(xor16_sum(v));
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) {

@@ -63,9 +63,12 @@ def test_split_rule_and_workspace_sizes(L):
     assert wsvd.append_workspace_bytes(64, 4096, 32, 48) >= 64 * 2 * 32 * 48 * 4
 
 
-# fake, well-aligned device addresses: validation must reject before use
+# Fake, well-aligned device addresses: validation must reject before use.
+# Every helper defaults to a workspace that is too small, so a case that
+# passed the check it targets would stop at WSVD_ERR_WORKSPACE instead of
+# launching a kernel on fake pointers.
 P = 0x7F0000000000
-WS = 1 << 24
+WS = 16
 
 
 def decode(L, **kw):
@@ -114,7 +117,7 @@ def test_combine_rejects(L):
 
 def append(L, **kw):
     a = dict(nb=64, E=4096, nh=32, r=48, L_cap=8192, x=P, x_dt=BF16, A_K=P, A_V=P, A_dt=BF16, pos=P, C_K=P,
-             C_V=P, C_dt=BF16, s_K=None, s_V=None, ws=P, ws_bytes=1 << 30)
+             C_V=P, C_dt=BF16, s_K=None, s_V=None, ws=P, ws_bytes=WS)
     a.update(kw)
     v = ctypes.c_void_p
     return L.wsvd_append_latent(a["nb"], a["E"], a["nh"], a["r"], a["L_cap"], v(a["x"]), a["x_dt"], v(a["A_K"]),
