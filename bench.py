@@ -163,6 +163,59 @@ def load_traffic(workload_name, launches_bytes):
 
 
 # ---------------------------------------------------------------------------
+# dense Flash-Decoding baseline at the same shape (the pages' comparison)
+# ---------------------------------------------------------------------------
+def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
+    """Time the WSVD decode step and dense Flash-Decoding on equal shapes.
+
+    Random GPU-side bf16 inputs (timing only; parity is covered by the
+    tests), cold-HBM rotation for both, graph replay of `steps` steps.
+    L is an int or an int array [nb]; the cache capacity is max(L).
+    """
+    import numpy as np
+    import torch
+    from rank_kv_cache_flash_amd import wsvd
+
+    Ls = np.broadcast_to(np.asarray(L, dtype=np.int64), (nb,))
+    L_cap = int(Ls.max())
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    bf = torch.bfloat16
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda") * scale).to(bf)
+
+    def copies_for(nbytes):
+        return max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
+
+    wb = int(Ls.sum()) * nh * 2 * r * 2 + nh * 2 * r * H * 2 + nb * nh * H * 4
+    db = int(Ls.sum()) * nh * 2 * H * 2 + nb * nh * H * 4
+    Lt = torch.tensor(Ls.astype(np.int32), device="cuda")
+    ws = wsvd.decode_workspace(nb, nh, H, L_cap, 0)
+    ws2 = wsvd.decode_workspace(nb, nh, H, L_cap, 0)
+    out = torch.empty(nb, nh, H, dtype=bf, device="cuda")
+    w_calls, d_calls = [], []
+    for _ in range(copies_for(wb)):
+        q = rnd(nb, nh, H, scale=H ** -0.5)
+        CK, CV = rnd(nb, nh, L_cap, r, scale=r ** -0.5), rnd(nb, nh, L_cap, r, scale=r ** -0.5)
+        BK, BV = rnd(nh, r, H, scale=H ** -0.5), rnd(nh, r, H, scale=H ** -0.5)
+        w_calls.append(wsvd.PreparedDecode(q, CK, CV, BK, BV, Lt, workspace=ws, out=out))
+    t_w = graph_time(lambda i: w_calls[i % len(w_calls)](), steps, warmup)[0]
+    del w_calls
+    torch.cuda.empty_cache()
+    for _ in range(copies_for(db)):
+        q = rnd(nb, nh, H, scale=H ** -0.5)
+        K, V = rnd(nb, nh, L_cap, H, scale=H ** -0.5), rnd(nb, nh, L_cap, H, scale=H ** -0.5)
+        d_calls.append(wsvd.PreparedDense(q, K, V, Lt, workspace=ws2, out=out))
+    t_d = graph_time(lambda i: d_calls[i % len(d_calls)](), steps, warmup)[0]
+    del d_calls
+    torch.cuda.empty_cache()
+    return {"nb": nb, "nh": nh, "H": H, "r": r, "L_sum": int(Ls.sum()), "L_cap": L_cap,
+            "wsvd_us": round(t_w * 1e6, 3), "dense_us": round(t_d * 1e6, 3),
+            "speedup": round(t_d / t_w, 3), "byte_ratio": round(db / wb, 3),
+            "wsvd_GB_per_s": round(wb / t_w / 1e9, 1), "dense_GB_per_s": round(db / t_d / 1e9, 1)}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host (bounded sample)
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, gpu_out, budget_s=12.0):
@@ -262,7 +315,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--mode", choices=["bench", "decode-loop", "copy-calib", "counters"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "decode-loop", "copy-calib", "counters", "dense-sweep"],
+                    default="bench",
                     help="decode-loop / copy-calib / counters: plain launch loops for counter collection")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
@@ -291,6 +345,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy-calib", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+        return
+    if args.mode == "dense-sweep":
+        # WSVD decode vs dense Flash-Decoding over sequence length and batch
+        # (32 heads, H = 128, r = 32 and 64); one JSON line per point.
+        for r in (32, 64):
+            for nb in (1, 8, 32):
+                for L in (1024, 4096, 16384, 32768):
+                    steps = max(10, min(400, int(2e-2 / max(nb * 32 * L * 2 * 128 * 2 / 6e12, 1e-7))))
+                    rec = dense_vs_wsvd(nb, 32, 128, r, L, steps)
+                    rec["steps"] = steps
+                    print(json.dumps(rec), flush=True)
         return
     if args.mode == "counters":
         # 1) a plain device copy of known size (calibrates FETCH_SIZE / WRITE_SIZE),
@@ -345,6 +410,10 @@ def main():
         torch.cuda.synchronize()
         cpu, parity = cpu_baseline(w, w.out, budget_s=args.cpu_budget)
 
+    vs_dense = None
+    if not cfg.has_append and cfg.C_dt == "bf16":
+        vs_dense = dense_vs_wsvd(cfg.nb, cfg.nh, cfg.H, cfg.r, cfg.L, args.steps, min(args.warmup, 10))
+
     per = {}
     also = [int(x) for x in args.also.split(",") if x.strip()] if args.also else []
     del w
@@ -380,6 +449,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_max_rel_err_vs_oracle": parity,
+        "vs_dense_flash_decoding": vs_dense,
         "per_config": per,
         "kernel_src": kernel_src_hash(),
     }

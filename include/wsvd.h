@@ -180,6 +180,29 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/*
+ * wsvd_dense_decode_attn -- the speed baseline the pages compare WSVD with:
+ * ordinary Flash-Decoding attention over full K and V (Japanese page
+ * section 4, German page section 4: decode latency against Flash Decoding).
+ * Same split rule, partial format, in-kernel merge and workspace as
+ * wsvd_decode_attn; it exists so both can be timed on the same device.
+ *
+ *     out[b,h,:] = softmax(sigma * K[b,h,:l,:] q[b,h,:]) V[b,h,:l,:],  l = L[b]
+ *
+ *   K, V, kv_dt   [nb, nh, L_cap, H] BF16 (H in {64, 128})
+ *   workspace     wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits)
+ *                 bytes, counter area zero before first use (as above)
+ *   other arguments as for wsvd_decode_attn.
+ */
+int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap,
+                           const int32_t* L,
+                           const void* q, wsvd_dtype q_dt,
+                           const void* K, const void* V, wsvd_dtype kv_dt,
+                           float softmax_scale, int n_splits,
+                           void* workspace, size_t workspace_bytes,
+                           void* out, wsvd_dtype out_dt,
+                           hipStream_t stream);
+
 /* Splits wsvd_decode_attn uses for these sizes (n_splits > 0 is returned
  * unchanged; 0 selects the automatic choice).  Pure host function.
  * Returns a negative wsvd_status for invalid sizes. */

@@ -147,6 +147,47 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, 
     return wsvd::launch_decode_split(a, H, r, C_dt, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
+int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap, const int32_t* L, const void* q, wsvd_dtype q_dt,
+                           const void* K, const void* V, wsvd_dtype kv_dt, float softmax_scale, int n_splits,
+                           void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt,
+                           hipStream_t stream) {
+    if (nb <= 0 || nh <= 0 || H <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
+    if ((long long)nb * nh * L_cap * H > (1ll << 46)) return WSVD_ERR_SHAPE;
+    if (!L || !q || !K || !V) return WSVD_ERR_NULL;
+    if (!act_dtype_ok(q_dt) || kv_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
+    if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
+    if (!head_dim_ok(H)) return WSVD_ERR_UNSUPPORTED;
+    if (!aligned16(L) || !aligned16(q) || !aligned16(K) || !aligned16(V) || (out && !aligned16(out)))
+        return WSVD_ERR_ALIGN;
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0) return WSVD_ERR_SHAPE;
+    if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+
+    wsvd::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.nb = nb;
+    a.nh = nh;
+    a.L_cap = L_cap;
+    a.S = S;
+    a.L = L;
+    a.q = q;
+    a.q_dt = q_dt;
+    a.C_K = K;
+    a.C_V = V;
+    a.B_dt = WSVD_BF16;
+    const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
+    a.scale_log2 = sigma * wsvd::kLog2e;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
+    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                             wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits));
+    a.out = out;
+    a.out_dt = out ? (int)out_dt : 0;
+    return wsvd::launch_dense_split(a, H, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
 int wsvd_combine_splits(int nb, int nh, int H, int n_splits, const float* o_part, const float* lse_part, void* out,
                         wsvd_dtype out_dt, hipStream_t stream) {
     if (nb <= 0 || nh <= 0 || H <= 0 || n_splits <= 0) return WSVD_ERR_SHAPE;

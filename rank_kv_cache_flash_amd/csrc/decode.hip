@@ -138,8 +138,11 @@ __device__ __forceinline__ float load_q_elem(const void* q, int q_dt, size_t idx
     return wide ? __uint_as_float(w) : (q_dt == WSVD_BF16 ? fb : fh);
 }
 
-template <int H, int R, int CT, int BT, int U>
+// DENSE = true is the comparison baseline: ordinary Flash-Decoding over full
+// K / V rows (r = H, no factors): q' is q itself and the partial is o / l.
+template <int H, int R, int CT, int BT, int U, bool DENSE = false>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+    static_assert(!DENSE || R == H, "dense rows are H wide");
     using T = CacheTraits<CT>;
     constexpr int EPC = T::EPC;
     constexpr int G = R / EPC;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     constexpr bool I8 = (CT == WSVD_I8);
     constexpr int BES = (BT == WSVD_F32) ? 4 : 2;  // factor element bytes
     constexpr int BEPC = 16 / BES;                 // factor elements per chunk
-    constexpr int NBC = R * H / BEPC;              // chunks per factor
+    constexpr int NBC = DENSE ? 1 : R * H / BEPC;  // chunks per factor
     constexpr int NBT = (NBC + 255) / 256;         // chunks per thread
     constexpr int CPR = H / BEPC;                  // chunks per factor row
     constexpr int NPART = 256 / H;                 // projection: threads per output
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < NBT; ++k) {
             const int c = tid + 256 * k;
-            if (NBC % 256 == 0 || c < NBC) {
+            if (!DENSE && (NBC % 256 == 0 || c < NBC)) {
                 bk[k] = *reinterpret_cast<const u32x4*>(bk_base + (size_t)c * 16);
                 bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
             }
@@ -248,11 +251,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
         // ---- q' = (sigma log2 e) B_K q from the chunks in registers ------------
         if (tid < H) sh_q[tid] = qv;
+        if (DENSE && tid < H) sh_qp[tid] = qv * a.scale_log2;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < NBT; ++k) {
             const int c = tid + 256 * k;
-            if (NBC % 256 == 0 || c < NBC) {
+            if (!DENSE && (NBC % 256 == 0 || c < NBC)) {
                 const int col = (c % CPR) * BEPC;
                 float p = 0.f;
 #pragma unroll
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             }
         }
         __syncthreads();
-        if (tid < R) {
+        if (!DENSE && tid < R) {
             float p = 0.f;
 #pragma unroll
             for (int c = 0; c < CPR; ++c) p += sh_qpart[tid * CPR + c];
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             sh_on[tid] = o / Lt;
         }
         __syncthreads();
-        {
+        if constexpr (!DENSE) {
             const int jj = tid % H;
             const int part = tid / H;
             constexpr int RP = R / NPART;
@@ -391,8 +395,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         __syncthreads();
         if (tid < H) {
             float o = 0.f;
+            if constexpr (DENSE) {
+                o = sh_on[tid];
+            } else {
 #pragma unroll
-            for (int p = 0; p < NPART; ++p) o += sh_proj[p * H + tid];
+                for (int p = 0; p < NPART; ++p) o += sh_proj[p * H + tid];
+            }
             store_coherent(o_out + tid, o);
             if (S == 1 && a.out) store_elem(a.out, a.out_dt, bh * H + tid, o);
         }
@@ -500,6 +508,23 @@ static hipError_t launch_h(const DecodeArgs& a, int r, int C_dt, hipStream_t st)
         case 64: return launch_hr<H, 64>(a, C_dt, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_dense_split(const DecodeArgs& a, int H, hipStream_t st) {
+    const unsigned nblk = (unsigned)((size_t)a.nb * a.nh * a.S);
+    switch (H) {
+        case 64:
+            hipLaunchKernelGGL((decode_split_kernel<64, 64, WSVD_BF16, WSVD_BF16, 4, true>), dim3(nblk), dim3(256), 0,
+                               st, a);
+            break;
+        case 128:
+            hipLaunchKernelGGL((decode_split_kernel<128, 128, WSVD_BF16, WSVD_BF16, 4, true>), dim3(nblk), dim3(256),
+                               0, st, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipStream_t st) {

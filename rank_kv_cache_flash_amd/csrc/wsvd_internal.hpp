@@ -31,6 +31,9 @@ struct DecodeArgs {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipStream_t st);
 
+// Dense Flash-Decoding baseline (bf16 K / V rows of H values, no factors).
+hipError_t launch_dense_split(const DecodeArgs& a, int H, hipStream_t st);
+
 hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, const float* lse_part,
                           void* out, int out_dt, hipStream_t st);
 

@@ -39,6 +39,8 @@ def lib() -> ctypes.CDLL:
     L.wsvd_decode_attn.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32,
                                    f32, i32, vp, sz, vp, i32, vp]
     L.wsvd_decode_attn.restype = i32
+    L.wsvd_dense_decode_attn.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, f32, i32, vp, sz, vp, i32, vp]
+    L.wsvd_dense_decode_attn.restype = i32
     L.wsvd_combine_splits.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
     L.wsvd_combine_splits.restype = i32
     L.wsvd_append_latent.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, vp,
@@ -157,6 +159,42 @@ def decode_attn(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=N
     o_part = wsb[: nb * nh * S * H * 4].view(torch.float32).view(nb, nh, S, H)
     lse_part = wsb[off: off + nb * nh * S * 4].view(torch.float32).view(nb, nh, S)
     return out, o_part, lse_part
+
+
+def dense_decode_attn(q, K, V, L, *, softmax_scale=None, n_splits=None, out=None, out_dtype=None, workspace=None,
+                      stream=None):
+    """wsvd_dense_decode_attn (Flash-Decoding baseline): q [nb, nh, H]; K / V [nb, nh, L_cap, H] bf16."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V"), (L, "L"), (out, "out"), (workspace, "workspace")):
+        _dev(t, n)
+    nb, nh, H = q.shape
+    L_cap = K.shape[2]
+    if workspace is None:
+        workspace = decode_workspace(nb, nh, H, L_cap, n_splits or 0, device=q.device)
+    if out is None:
+        out = torch.empty((nb, nh, H), dtype=out_dtype or q.dtype, device=q.device)
+    st = lib().wsvd_dense_decode_attn(nb, nh, H, L_cap, _ptr(L), _ptr(q), _DT[q.dtype], _ptr(K), _ptr(V),
+                                      _DT[K.dtype], float(softmax_scale or 0.0), int(n_splits or 0), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _ptr(out), _DT[out.dtype],
+                                      _stream(stream))
+    _check(st, "wsvd_dense_decode_attn")
+    return out
+
+
+class PreparedDense:
+    """wsvd_dense_decode_attn with fixed buffers; __call__(stream) enqueues it."""
+
+    def __init__(self, q, K, V, L, *, workspace, out, n_splits=None):
+        for t, n in ((q, "q"), (K, "K"), (V, "V"), (L, "L"), (out, "out"), (workspace, "workspace")):
+            _dev(t, n)
+        nb, nh, H = q.shape
+        self._keep = (q, K, V, L, workspace, out)
+        self._args = (nb, nh, H, K.shape[2], _ptr(L), _ptr(q), _DT[q.dtype], _ptr(K), _ptr(V), _DT[K.dtype], 0.0,
+                      int(n_splits or 0), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                      _DT[out.dtype])
+        self._fn = lib().wsvd_dense_decode_attn
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)), "wsvd_dense_decode_attn")
 
 
 def combine_splits(o_part, lse_part, *, out=None, out_dtype=torch.float32, stream=None):

@@ -144,3 +144,25 @@ def test_binding_refuses_cpu_tensors(L):
     b = torch.zeros(4, 16, 64)
     with pytest.raises(ValueError, match="GPU"):
         wsvd.decode_attn(q, c, c, b, b, torch.zeros(1, dtype=torch.int32))
+
+
+def dense(L, **kw):
+    a = dict(nb=2, nh=4, H=128, L_cap=256, Lp=P, q=P, q_dt=BF16, K=P, V=P, kv_dt=BF16, S=0, ws=P, ws_bytes=WS,
+             out=P, out_dt=BF16)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return L.wsvd_dense_decode_attn(a["nb"], a["nh"], a["H"], a["L_cap"], v(a["Lp"]), v(a["q"]), a["q_dt"], v(a["K"]),
+                                    v(a["V"]), a["kv_dt"], 0.0, a["S"], v(a["ws"]), a["ws_bytes"], v(a["out"]),
+                                    a["out_dt"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), ESHAPE), (dict(L_cap=-1), ESHAPE), (dict(S=-2), ESHAPE),
+    (dict(K=None), ENULL), (dict(Lp=None), ENULL),
+    (dict(kv_dt=F32), EDTYPE), (dict(kv_dt=I8), EDTYPE), (dict(q_dt=I8), EDTYPE),
+    (dict(H=96), EUNSUP), (dict(H=32), EUNSUP),
+    (dict(V=P + 4), EALIGN), (dict(q=P + 2), EALIGN),
+    ({}, EWS), (dict(ws=None), EWS),
+])
+def test_dense_rejects(L, kw, want):
+    assert dense(L, **kw) == want

@@ -317,3 +317,37 @@ def test_merge_across_xcds_repeated(W):
     for o in outs:
         assert torch.equal(o, ref)
     check("merge across XCDs", f64(ref), O.decode_attn(inp), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# dense Flash-Decoding baseline: the oracle with r = H and identity factors
+# ---------------------------------------------------------------------------
+def _dense_case(nb, nh, H, L, L_cap, seed, q_gain=1.0):
+    inp = I.make_decode_inputs(nb, nh, H, H, L, L_cap, seed=seed, act_dt="bf16", C_dt="bf16", q_gain=q_gain)
+    eye = np.zeros((nh, H, H), np.uint16)
+    eye[:, np.arange(H), np.arange(H)] = 0x3F80          # bf16 1.0
+    inp.B_K = eye
+    inp.B_V = eye.copy()
+    return inp
+
+
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("S", [None, 1, 3])
+def test_dense_baseline_matches_oracle(W, H, S):
+    L = np.array([300, 1, 0, 257, 129], np.int32)
+    inp = _dense_case(5, 3, H, L, 300, seed=55 + H, q_gain=2.0 * H)
+    d = W.device_inputs(inp)
+    out = W.dense_decode_attn(d["q"], d["C_K"], d["C_V"], d["L"], n_splits=S)
+    torch.cuda.synchronize()
+    g = f64(out)
+    check(f"dense H={H} S={S}", g, O.decode_attn(inp), TOL["bf16"])
+    assert not g[2].any()
+
+
+def test_dense_baseline_full_llava_layer(W):
+    """LLaVA-7B layer shape (1 x 32 heads, H = 128, L = 1088) with full K / V."""
+    inp = _dense_case(1, 32, 128, 1088, 1088, seed=2002, q_gain=4.0 * 128)
+    d = W.device_inputs(inp)
+    out = W.dense_decode_attn(d["q"], d["C_K"], d["C_V"], d["L"])
+    torch.cuda.synchronize()
+    check("dense llava layer", f64(out), O.decode_attn(inp), TOL["bf16"])
