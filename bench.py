@@ -82,8 +82,7 @@ class Workload:
             kw = dict(s_K=d.get("s_K"), s_V=d.get("s_V"), n_splits=n_splits)
             steps = []
             if cfg.has_append:
-                aw = torch.empty(wsvd.append_workspace_bytes(nb, cfg.E, nh, cfg.r), dtype=torch.uint8,
-                                 device="cuda")
+                aw = wsvd.append_workspace(nb, cfg.E, nh, cfg.r)
                 d["_aws"] = aw
                 steps.append(wsvd.PreparedAppend(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"],
                                                  workspace=aw))

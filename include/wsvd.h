@@ -169,7 +169,14 @@ int wsvd_combine_splits(int nb, int nh, int H, int n_splits,
  *   C_K, C_V, C_dt   [nb, nh, L_cap, r]
  *   s_K, s_V         unused (must be NULL) for BF16/F32 caches
  *   workspace        device scratch of wsvd_append_workspace_bytes(...)
- *                    bytes (fp32 split-E partial products), 256-byte aligned
+ *                    bytes, 256-byte aligned: fp32 split-E partial tiles
+ *                    and one arrival counter per output tile.  It must be
+ *                    zero-filled before its first use; every call leaves
+ *                    the counters zero again, so calls issued one after
+ *                    another on a stream may share it (concurrent calls on
+ *                    different streams need separate workspaces).  When
+ *                    the size function returns 0 no split is used and
+ *                    workspace may be NULL.
  */
 int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap,
                        const void* x, wsvd_dtype x_dt,
@@ -218,7 +225,9 @@ size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits);
  * workspace.  Pure host. */
 size_t wsvd_decode_counter_offset(int nb, int nh, int H, int L_cap, int n_splits);
 
-/* Workspace bytes wsvd_append_latent needs (0 on invalid sizes).  Pure host. */
+/* Workspace bytes wsvd_append_latent needs: 0 on invalid sizes, and 0 when
+ * the sizes need no E split (then the workspace argument may be NULL).
+ * Pure host. */
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r);
 
 /* Static description of a status code.  Pure host; never NULL. */

@@ -78,8 +78,9 @@ size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_split
 
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r) {
     if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0) return 0;
-    const int ks = wsvd::append_num_esplits(nb, E, nh, r);
-    return round_up((size_t)ks * nb * 2 * nh * r * sizeof(float), 256);
+    const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
+    if (part == 0) return 0;
+    return round_up(part, 256) + round_up((size_t)wsvd::append_num_tiles(nb, nh, r) * sizeof(unsigned), 256);
 }
 
 const char* wsvd_status_string(int st) {
@@ -216,7 +217,7 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
         !aligned16(C_V))
         return WSVD_ERR_ALIGN;
     const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
-    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+    if (need > 0 && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return WSVD_ERR_WORKSPACE;
 
     wsvd::AppendArgs a;
     a.nb = nb;
@@ -231,8 +232,10 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     a.C_K = C_K;
     a.C_V = C_V;
     a.C_dt = C_dt;
-    a.part = static_cast<float*>(workspace);
     a.KS = wsvd::append_num_esplits(nb, E, nh, r);
+    const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
+    a.part = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.counters = need > 0 ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + round_up(part, 256)) : nullptr;
     return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 

@@ -11,22 +11,38 @@
 // matrix cores (v_mfma_f32_16x16x32_bf16) so the arithmetic hides under
 // that stream.
 //
-// Kernel 1 (gemm): block = 64 rows of x  x  64 columns of A  x  one E-slice of
-// EC rows.  Enough E-slices are used to put >= 1.5 blocks on each CU.  A
-// arrives row-major (columns contiguous) but the MFMA B operand wants 8
-// consecutive k per lane, so each thread loads an 8 x 8 (k x n) bf16 block
-// with eight 16-byte loads (a wave covers 8 full 128-byte rows per load),
-// transposes it in registers and stores 8 k-contiguous vectors into LDS.
-// The LDS tile is [64 n][EC k] with a 16-byte row pad and the k-block index
-// xor-swizzled by n/8, so both the transposed stores and the fragment reads
-// are free of bank conflicts.  Each wave owns 16 rows of x and all 64
-// columns: 4 accumulators of 16 x 16.  The fp32 partial tile goes to the
-// workspace.
-// Kernel 2 (reduce + scatter): sums the E-slices in index order (so the
-// result is deterministic), rounds once to the cache dtype and writes row
-// pos[b] of every head's K and V cache.
+// One launch.  Block = 64 rows of x  x  64 columns of A  x  one E-slice;
+// enough E-slices (KS) are used to put >= 1.5 blocks on each CU.
+//  * A block requests two LDS stages (2 x 256 E rows of A and x) at once,
+//    one register buffer per stage.  With E = 4096 the split makes every
+//    slice exactly two stages, so the whole A stream is in flight at once
+//    and never waits on a dependent round trip.
+//  * A arrives row-major (columns contiguous) but the MFMA B operand wants 8
+//    consecutive k per lane, so each thread loads an 8 x 8 (k x n) bf16
+//    block with eight 16-byte loads (a wave covers 8 full 128-byte rows per
+//    load), transposes it in registers and stores 8 k-contiguous vectors
+//    into LDS.  The LDS tile is [64 n][256 k] with a 16-byte row pad and the
+//    k-block index xor-swizzled by n/8, so both the transposed stores and
+//    the fragment reads are free of bank conflicts.
+//  * x is read with whole-row loads (a wave covers two 512-byte row pieces
+//    per load) into a second padded LDS tile [64 m][256 k]; gathering the
+//    MFMA A fragments (16 rows x 16 bytes) straight from memory instead
+//    cost several times more L2 requests for the same bytes.
+//  * Each wave owns 16 rows of x and all 64 columns: 4 accumulators of
+//    16 x 16.
+//  * With KS > 1 each block writes its fp32 partial tile to the workspace
+//    (device-coherent 16-byte stores, in the accumulator's own lane order,
+//    so a wave writes 1 KB contiguous per store) and bumps
+//    the tile's arrival counter; the block that arrives last sums the KS
+//    partials in slice order (so the result does not depend on which block
+//    finished last), resets the counter, rounds once to the cache dtype and
+//    writes row pos[b] of every head's K and V cache.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
+
+#ifndef WSVD_APPEND_TARGET_BLOCKS
+#define WSVD_APPEND_TARGET_BLOCKS 384
+#endif
 
 namespace wsvd {
 
@@ -37,14 +53,97 @@ constexpr int AP_NT = 64;           // columns per block
 constexpr int AP_MT = 64;           // rows of x per block
 constexpr int AP_EC = 256;          // E rows per LDS stage
 constexpr int AP_PITCH = AP_EC + 8; // bf16 elements per LDS row (16-byte pad)
+constexpr int AP_TILE_VALS = AP_NT * AP_MT;  // fp32 values in one partial tile
 
 union V16 {
     u32x4 u;
     bf16x8 b;
 };
 
-__global__ __launch_bounds__(256) void append_gemm_kernel(AppendArgs a) {
+// One stage of operands in registers: this thread's 8 x 8 block of A and
+// its eight 16-byte pieces of x rows.
+struct Stage {
+    u32x4 a[8];
+    u32x4 x[8];
+};
+
+// Raw buffer descriptor over `bytes` bytes at p (gfx9 word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;     // cache-policy bit nt: streamed once
+constexpr int kCoherentAgent = 16;  // cache-policy bit sc1: device-coherent
+
+// Buffer loads keep one 32-bit lane offset per stream and put the uniform
+// part (stage start, row step) in a scalar offset, instead of a 64-bit
+// address per load.
+struct TileCtx {
+    __amdgpu_buffer_rsrc_t ra, rx;
+    uint32_t a_voff;     // bytes: (kblk * 8 * N1 + ncol) * 2
+    uint32_t a_row;      // bytes per row of A: N1 * 2
+    uint32_t x_voff[8];  // bytes: (xrow_i * E + xcol) * 2
+};
+
+__device__ __forceinline__ void load_stage(Stage& s, const TileCtx& c, int es) {
+    // Columns past N1 read column 0 and rows past nb read row nb - 1 instead
+    // (in bounds); those outputs are never written, and an output column
+    // (row) depends only on its own column of A (row of x).
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        s.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.a_voff, (es + i) * c.a_row, kNonTemporal);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.x[i] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_voff[i], es * 2, 0);
+}
+
+// Transpose the stage's A block into LDS, stage x rows beside it, and run
+// the stage's MFMAs.
+__device__ __forceinline__ void mma_stage(const Stage& s, uint16_t* sB, uint16_t* sX, f32x4 (&acc)[4], int tid,
+                                          int lane, int wave) {
+    const int nblk = tid & 7;
+    const int kblk = tid >> 3;
+    // 8 x 8 transpose: tr[n'] holds k = 0..7 of column n'.
+    u32x4 tr[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t r0 = s.a[2 * p][w], r1 = s.a[2 * p + 1][w];
+            tr[2 * w][p] = (r0 & 0xffffu) | (r1 << 16);
+            tr[2 * w + 1][p] = (r0 >> 16) | (r1 & 0xffff0000u);
+        }
+    }
+    __syncthreads();  // the previous stage's fragment reads are done
+#pragma unroll
+    for (int np = 0; np < 8; ++np) {
+        const int n = nblk * 8 + np;
+        const int kb = kblk ^ (nblk & 7);
+        *reinterpret_cast<u32x4*>(&sB[n * AP_PITCH + kb * 8]) = tr[np];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(&sX[((tid >> 5) + 8 * i) * AP_PITCH + (tid & 31) * 8]) = s.x[i];
+    __syncthreads();
+    const uint16_t* xr = sX + (wave * 16 + (lane & 15)) * AP_PITCH + (lane >> 4) * 8;
+#pragma unroll
+    for (int st = 0; st < AP_EC / 32; ++st) {
+        V16 xf;
+        xf.u = *reinterpret_cast<const u32x4*>(xr + st * 32);
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const int n = jn * 16 + (lane & 15);
+            const int kb = (st * 4 + (lane >> 4)) ^ ((n >> 3) & 7);
+            V16 bf;
+            bf.u = *reinterpret_cast<const u32x4*>(&sB[n * AP_PITCH + kb * 8]);
+            acc[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf.b, bf.b, acc[jn], 0, 0, 0);
+        }
+    }
+}
+
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sB[AP_NT * AP_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sX[AP_MT * AP_PITCH];
+    __shared__ int sh_last;
 
     const int N1 = a.nh * a.r;
     const int n0 = blockIdx.x * AP_NT;
@@ -53,125 +152,140 @@ __global__ __launch_bounds__(256) void append_gemm_kernel(AppendArgs a) {
     const int ks = blockIdx.z;
     const int e_len = a.E / a.KS;
     const int e_beg = ks * e_len;
-    const uint16_t* A = kv ? a.A_V : a.A_K;
+    const int ns = e_len / AP_EC;
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // loader role: 8 x 8 block (k rows kblk*8.., n cols nblk*8..)
-    const int nblk = tid & 7;
-    const int kblk = tid >> 3;  // 0..31
-    const int ncol = n0 + nblk * 8;
-    const bool col_ok = ncol < N1;  // N1 is a multiple of 16
-
-    // MFMA role
-    const int mrow = m0 + wave * 16 + (lane & 15);
-    const bool row_ok = mrow < a.nb;
-    const int kq = (lane >> 4) * 8;  // this lane's k offset inside a 32-wide step
+    TileCtx c;
+    c.ra = make_rsrc(kv ? a.A_V : a.A_K, (uint32_t)((size_t)a.E * N1 * 2));
+    c.rx = make_rsrc(a.x, (uint32_t)((size_t)a.nb * a.E * 2));
+    int ncol = n0 + (tid & 7) * 8;
+    if (ncol >= N1) ncol = 0;  // N1 is a multiple of 16, chunks are 8 wide
+    c.a_row = (uint32_t)N1 * 2u;
+    c.a_voff = ((uint32_t)(tid >> 3) * 8u * (uint32_t)N1 + (uint32_t)ncol) * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        c.x_voff[i] = ((uint32_t)min(m0 + (tid >> 5) + 8 * i, a.nb - 1) * (uint32_t)a.E + (tid & 31) * 8u) * 2u;
 
     f32x4 acc[4];
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int es = e_beg; es < e_beg + e_len; es += AP_EC) {
-        // ---- global -> registers -------------------------------------------
-        u32x4 blk[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const size_t e = (size_t)es + kblk * 8 + i;
-            blk[i] = col_ok ? load16_stream(A + e * N1 + ncol) : u32x4{0u, 0u, 0u, 0u};
-        }
-        V16 xf[AP_EC / 32];
-#pragma unroll
-        for (int st = 0; st < AP_EC / 32; ++st) {
-            xf[st].u = row_ok ? *reinterpret_cast<const u32x4*>(a.x + (size_t)mrow * a.E + es + st * 32 + kq)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
-        // ---- 8 x 8 transpose: out[n'] holds k = 0..7 of column n' ------------
-        u32x4 tr[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t r0 = blk[2 * p][w], r1 = blk[2 * p + 1][w];
-                tr[2 * w][p] = (r0 & 0xffffu) | (r1 << 16);
-                tr[2 * w + 1][p] = (r0 >> 16) | (r1 & 0xffff0000u);
-            }
-        }
-        __syncthreads();  // previous stage's readers are done
-#pragma unroll
-        for (int np = 0; np < 8; ++np) {
-            const int n = nblk * 8 + np;
-            const int kb = kblk ^ (nblk & 7);
-            *reinterpret_cast<u32x4*>(&sB[n * AP_PITCH + kb * 8]) = tr[np];
-        }
-        __syncthreads();
-        // ---- MFMA over the stage ----------------------------------------------
-#pragma unroll
-        for (int st = 0; st < AP_EC / 32; ++st) {
-#pragma unroll
-            for (int jn = 0; jn < 4; ++jn) {
-                const int n = jn * 16 + (lane & 15);
-                const int kb = (st * 4 + (lane >> 4)) ^ ((n >> 3) & 7);
-                V16 bf;
-                bf.u = *reinterpret_cast<const u32x4*>(&sB[n * AP_PITCH + kb * 8]);
-                acc[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[st].b, bf.b, acc[jn], 0, 0, 0);
-            }
-        }
+    // Two stages (512 E rows) requested together; the split factor keeps a
+    // block's slice at one or two stages, so one pass normally covers it.
+    Stage s0, s1;
+    for (int st = 0; st < ns; st += 2) {
+        load_stage(s0, c, e_beg + st * AP_EC);
+        if (st + 1 < ns) load_stage(s1, c, e_beg + (st + 1) * AP_EC);
+        mma_stage(s0, sB, sX, acc, tid, lane, wave);
+        if (st + 1 < ns) mma_stage(s1, sB, sX, acc, tid, lane, wave);
     }
 
-    // ---- partial tile -> workspace: part[ks][m][kv*N1 + n] ------------------
-    const int N2 = 2 * N1;
+    // Rows of the caches this lane's accumulator entries go to (requested
+    // only once the tile is complete, beside the last round of loads).
+    int prow[4];
+    auto load_pos = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wave * 16 + (lane >> 4) * 4 + i;
+            prow[i] = (m < a.nb) ? a.pos[m] : -1;
+        }
+    };
+
+    if (a.KS > 1) {
+        // Partial tile in accumulator lane order: accumulator jn of thread t
+        // is the 16 bytes at float index ((ks * 4 + jn) * 256 + t) * 4 of the
+        // tile's KS-slice area.
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.part + (size_t)tile * a.KS * AP_TILE_VALS, (uint32_t)(a.KS * AP_TILE_VALS * sizeof(float)));
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[jn]), rs,
+                                                   ((ks * 4 + jn) * 256 + tid) * 16, 0, kCoherentAgent);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            sh_last = (__hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (unsigned)(a.KS - 1));
+        __syncthreads();
+        if (!sh_last) return;
+        load_pos();
+
+        // Last arrival: ordered sum over the KS slices, 8 slices per round
+        // trip (all loads of a round are issued before any is used).
+        f32x4 sum[4];
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) sum[jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < a.KS; k0 += 8) {
+            f32x4 v[8][4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = min(k0 + u, a.KS - 1);
+#pragma unroll
+                for (int jn = 0; jn < 4; ++jn)
+                    v[u][jn] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((k * 4 + jn) * 256 + tid) * 16, 0,
+                                                                     kCoherentAgent));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (k0 + u < a.KS) {
+#pragma unroll
+                    for (int jn = 0; jn < 4; ++jn) sum[jn] += v[u][jn];
+                }
+            }
+        }
+        if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[jn] = sum[jn];
+    } else {
+        load_pos();
+    }
+
+    // Round once and scatter into the caches.
+    void* C = kv ? a.C_V : a.C_K;
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
         const int n = n0 + jn * 16 + (lane & 15);
         if (n >= N1) continue;
+        const int h = n / a.r;
+        const int col = n - h * a.r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = m0 + wave * 16 + (lane >> 4) * 4 + i;
-            if (m < a.nb) a.part[((size_t)ks * a.nb + m) * N2 + kv * N1 + n] = acc[jn][i];
+            const int p = prow[i];
+            if (m >= a.nb || p < 0 || p >= a.L_cap) continue;
+            const size_t off = (((size_t)m * a.nh + h) * a.L_cap + p) * a.r + col;
+            store_elem_wt(C, a.C_dt, off, acc[jn][i]);
         }
     }
 }
 
-__global__ __launch_bounds__(256) void append_scatter_kernel(AppendArgs a) {
-    const int N1 = a.nh * a.r;
-    const int N2 = 2 * N1;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.nb * N2) return;
-    const int b = (int)(idx / N2);
-    const int n = (int)(idx % N2);
-    const int p = a.pos[b];
-    if (p < 0 || p >= a.L_cap) return;
-    float v = 0.f;
-    for (int ks = 0; ks < a.KS; ++ks) v += a.part[((size_t)ks * a.nb + b) * N2 + n];
-    const int kv = n >= N1;
-    const int nn = n - kv * N1;
-    const int h = nn / a.r;
-    const int i = nn % a.r;
-    void* C = kv ? a.C_V : a.C_K;
-    const size_t off = (((size_t)b * a.nh + h) * a.L_cap + p) * a.r + i;
-    store_elem(C, a.C_dt, off, v);
-}
-
 int append_num_esplits(int nb, int E, int nh, int r) {
-    // Blocks without E-splitting: column tiles x {K, V} x row tiles.
-    const long ntile = (long)((nh * r + AP_NT - 1) / AP_NT) * 2 * ((nb + AP_MT - 1) / AP_MT);
+    const long ntile = append_num_tiles(nb, nh, r);
     int ks = 1;
     // >= 1.5 blocks per CU (256 CUs), E-slices a multiple of the LDS stage.
-    while (ntile * ks < 384 && E % (2 * ks * AP_EC) == 0) ks *= 2;
+    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2 * ks * AP_EC) == 0) ks *= 2;
     return ks;
+}
+
+long append_num_tiles(int nb, int nh, int r) {
+    return (long)((nh * r + AP_NT - 1) / AP_NT) * 2 * ((nb + AP_MT - 1) / AP_MT);
+}
+
+size_t append_partial_bytes(int nb, int E, int nh, int r) {
+    const int ks = append_num_esplits(nb, E, nh, r);
+    if (ks <= 1) return 0;
+    return (size_t)append_num_tiles(nb, nh, r) * ks * AP_TILE_VALS * sizeof(float);
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     const int N1 = a.nh * a.r;
-    dim3 g1((N1 + AP_NT - 1) / AP_NT, 2 * ((a.nb + AP_MT - 1) / AP_MT), a.KS);
-    hipLaunchKernelGGL(append_gemm_kernel, g1, dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t tot = (size_t)a.nb * 2 * N1;
-    hipLaunchKernelGGL(append_scatter_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a);
+    dim3 g((N1 + AP_NT - 1) / AP_NT, 2 * ((a.nb + AP_MT - 1) / AP_MT), a.KS);
+    hipLaunchKernelGGL(append_kernel, g, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int nbh, int H, int S, con
         }
     }
     const float v = (wsum > 0.f) ? acc / wsum : 0.f;
-    store_elem(out, out_dt, (size_t)row * H + t, v);
+    store_elem_wt(out, out_dt, (size_t)row * H + t, v);
 }
 
 hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, const float* lse_part, void* out,

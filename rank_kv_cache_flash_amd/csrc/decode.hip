@@ -402,13 +402,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 for (int p = 0; p < NPART; ++p) o += sh_proj[p * H + tid];
             }
             store_coherent(o_out + tid, o);
-            if (S == 1 && a.out) store_elem(a.out, a.out_dt, bh * H + tid, o);
+            if (S == 1 && a.out) store_elem_wt(a.out, a.out_dt, bh * H + tid, o);
         }
         lse_out = (M + fast_log2(Lt)) * kLn2;
     } else {
         for (int i = tid; i < H; i += 256) {
             store_coherent(o_out + i, 0.f);
-            if (S == 1 && a.out) store_elem(a.out, a.out_dt, bh * H + i, 0.f);
+            if (S == 1 && a.out) store_elem_wt(a.out, a.out_dt, bh * H + i, 0.f);
         }
     }
     if (tid == 0) store_coherent(a.lse_part + bh * S + s, lse_out);
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             }
         }
     }
-    if (tid < H) store_elem(a.out, a.out_dt, bh * H + tid, wsum > 0.f ? accm / wsum : 0.f);
+    if (tid < H) store_elem_wt(a.out, a.out_dt, bh * H + tid, wsum > 0.f ? accm / wsum : 0.f);
     if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

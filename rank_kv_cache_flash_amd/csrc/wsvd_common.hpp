@@ -45,11 +45,23 @@ __device__ __forceinline__ float load_elem(const void* p, int dt, size_t i) {
     }
 }
 
-__device__ __forceinline__ void store_elem(void* p, int dt, size_t i, float v) {
+// Store `v` as element i of a tensor of runtime dtype `dt`, written through
+// to memory at device scope.  Results a kernel leaves behind go out this
+// way: a plain store leaves a dirty L2 line for the end-of-kernel release
+// to write back, which measured slower than storing through.
+__device__ __forceinline__ void store_elem_wt(void* p, int dt, size_t i, float v) {
     switch (dt) {
-        case WSVD_F32: static_cast<float*>(p)[i] = v; break;
-        case WSVD_BF16: static_cast<uint16_t*>(p)[i] = f32_to_bf16(v); break;
-        default: static_cast<uint16_t*>(p)[i] = f32_to_f16(v); break;
+        case WSVD_F32:
+            __hip_atomic_store(static_cast<float*>(p) + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        case WSVD_BF16:
+            __hip_atomic_store(static_cast<uint16_t*>(p) + i, f32_to_bf16(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        default:
+            __hip_atomic_store(static_cast<uint16_t*>(p) + i, f32_to_f16(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            break;
     }
 }
 

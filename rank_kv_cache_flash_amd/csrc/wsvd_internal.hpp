@@ -46,7 +46,8 @@ struct AppendArgs {
     void* C_K;
     void* C_V;
     int C_dt;
-    float* part;          // fp32 [KS, nb, 2*nh*r] split-E partial products
+    float* part;          // fp32 split-E partial tiles (KS > 1 only)
+    unsigned* counters;   // per-tile arrival counters, zero between calls
     int KS;               // number of E splits
 };
 
@@ -54,5 +55,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
 // Split-E factor the append kernel uses for these sizes (host).
 int append_num_esplits(int nb, int E, int nh, int r);
+// Output tiles (64 rows x 64 columns, K and V separately) (host).
+long append_num_tiles(int nb, int nh, int r);
+// Bytes of split-E partial tiles for these sizes, 0 when KS == 1 (host).
+size_t append_partial_bytes(int nb, int E, int nh, int r);
 
 }  // namespace wsvd

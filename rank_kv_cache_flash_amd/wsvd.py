@@ -97,6 +97,13 @@ def append_workspace_bytes(nb, E, nh, r) -> int:
     return int(lib().wsvd_append_workspace_bytes(nb, E, nh, r))
 
 
+def append_workspace(nb, E, nh, r, device="cuda"):
+    """Zero-filled append workspace (its tile counters must start at zero;
+    every call leaves them zero again, so calls issued one after another
+    on a stream can share one buffer)."""
+    return torch.zeros(max(append_workspace_bytes(nb, E, nh, r), 256), dtype=torch.uint8, device=device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -219,7 +226,7 @@ def append_latent(x, A_K, A_V, pos, C_K, C_V, *, workspace=None, stream=None):
     _, nh, L_cap, r = C_K.shape
     need = append_workspace_bytes(nb, E, nh, r)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = append_workspace(nb, E, nh, r, device=x.device)
     st = lib().wsvd_append_latent(nb, E, nh, r, L_cap, _ptr(x), _DT[x.dtype], _ptr(A_K), _ptr(A_V), _DT[A_K.dtype],
                                   _ptr(pos), _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], None, None, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))

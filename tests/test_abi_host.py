@@ -61,6 +61,7 @@ def test_split_rule_and_workspace_sizes(L):
     assert wsvd.decode_workspace_bytes(0, 1, 64, 1, 0) == 0
     assert wsvd.append_workspace_bytes(64, 4096, 32, 48) % 256 == 0
     assert wsvd.append_workspace_bytes(64, 4096, 32, 48) >= 64 * 2 * 32 * 48 * 4
+    assert wsvd.append_workspace_bytes(7, 768, 8, 16) == 0      # no E split: no scratch
 
 
 # Fake, well-aligned device addresses: validation must reject before use.

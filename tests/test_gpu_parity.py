@@ -284,6 +284,34 @@ def test_append_ranks(W, r):
     _append_case(W, inp)
 
 
+def test_append_row_tiles_and_reuse(W):
+    """70 sequences (two 64-row tiles, the second ragged), E split into 4
+    slices of two stages each; three calls on one workspace.  Equal inputs
+    give equal bits, and the third call (new token) is only right if every
+    tile counter came back to zero."""
+    inp = I.make_ragged_step_inputs(70, 4, 64, 32, 2048, 2, 20, 20, seed=77)
+    d = W.device_inputs(inp)
+    ws = W.append_workspace(70, 2048, 4, 32)
+    assert W.append_workspace_bytes(70, 2048, 4, 32) > 0
+    W.append_latent(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"], workspace=ws)
+    first = d["C_K"].clone(), d["C_V"].clone()
+    W.append_latent(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], d["C_K"]) and torch.equal(first[1], d["C_V"])
+    # a different token through the same workspace
+    inp2 = I.make_ragged_step_inputs(70, 4, 64, 32, 2048, 2, 20, 20, seed=78)
+    d2 = W.device_inputs(inp2)
+    W.append_latent(d2["x"], d2["A_K"], d2["A_V"], d2["pos"], d2["C_K"], d2["C_V"], workspace=ws)
+    torch.cuda.synchronize()
+    _, _, cK, cV = O.apply_append(inp2)
+    gK = d2["C_K"].view(torch.int16).cpu().numpy().view(np.uint16)
+    gV = d2["C_V"].view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(inp2.nb):
+        p = int(inp2.pos[b])
+        assert appended_row_ok(gK[b, :, p], cK[b], inp2.x[b:b + 1], inp2.A_K, inp2.nh, inp2.r).all()
+        assert appended_row_ok(gV[b, :, p], cV[b], inp2.x[b:b + 1], inp2.A_V, inp2.nh, inp2.r).all()
+
+
 def test_config5_full_step(W):
     c = CONFIGS[5]
     inp = c.make()
