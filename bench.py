@@ -314,9 +314,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--mode", choices=["bench", "decode-loop", "copy-calib", "counters", "dense-sweep"],
+    ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep"],
                     default="bench",
-                    help="decode-loop / copy-calib / counters: plain launch loops for counter collection")
+                    help="decode-loop / step-loop / copy-calib / counters: plain launch loops for traces and counters")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
@@ -373,6 +373,9 @@ def main():
             torch.cuda.synchronize()
             for i in range(args.steps):
                 w.decode_only(i)
+            if cfg.has_append:  # the append kernel alone, same count
+                for i in range(args.steps):
+                    w.full[i % w.copies][0]()
             torch.cuda.synchronize()
             rec["workloads"][cfg.name] = {"grid_blocks": w.cfg.nb * w.cfg.nh * w.S, "launches": args.steps,
                                           "alg_bytes_per_launch": int(w.decode_kernel_bytes), "splits": w.S}
@@ -380,13 +383,16 @@ def main():
             torch.cuda.empty_cache()
         print(json.dumps(rec))
         return
-    if args.mode == "decode-loop":
+    if args.mode in ("decode-loop", "step-loop"):
+        # Plain launch loops (no graph) for kernel traces: the split kernel
+        # alone (partials only, as timed for the roofline) or whole steps.
         cfg = CONFIGS[args.config]
         w = Workload(cfg, n_splits=args.splits or None)
+        fn = w.decode_only if args.mode == "decode-loop" else w.step
         for i in range(args.steps):
-            w.decode_only(i)
+            fn(i)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "decode-loop", "workload": cfg.name, "launches": args.steps,
+        print(json.dumps({"mode": args.mode, "workload": cfg.name, "launches": args.steps,
                           "decode_kernel_bytes": w.decode_kernel_bytes, "splits": w.S}))
         return
 
