@@ -126,16 +126,18 @@ __device__ __forceinline__ void chunk_axpy(const u32x4& d, float w, float* acc) 
     }
 }
 
-// q element as float from one unconditional dword load (dtype selected
-// arithmetically, no branch), so the prologue's loads stay straight-line.
-__device__ __forceinline__ float load_q_elem(const void* q, int q_dt, size_t idx) {
-    const bool wide = (q_dt == WSVD_F32);
-    const size_t word = wide ? idx : (idx >> 1);
-    const uint32_t w = static_cast<const uint32_t*>(q)[word];
+// q element idx: the dword holding it (one unconditional load, any dtype)
+// and, separately, its value.  Converting only after every other prologue
+// request is out keeps the first requests from waiting on this one.
+__device__ __forceinline__ uint32_t load_q_word(const void* q, int q_dt, size_t idx) {
+    const size_t word = (q_dt == WSVD_F32) ? idx : (idx >> 1);
+    return static_cast<const uint32_t*>(q)[word];
+}
+__device__ __forceinline__ float q_word_value(uint32_t w, int q_dt, size_t idx) {
     const uint16_t half = (idx & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
     const float fb = bf16_to_f32(half);
     const float fh = f16_to_f32(half);
-    return wide ? __uint_as_float(w) : (q_dt == WSVD_BF16 ? fb : fh);
+    return (q_dt == WSVD_F32) ? __uint_as_float(w) : (q_dt == WSVD_BF16 ? fb : fh);
 }
 
 // DENSE = true is the comparison baseline: ordinary Flash-Decoding over full
@@ -201,8 +203,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
     if (ntok > 0) {  // uniform over the block
         // ---- requests: q, B_K, B_V, first latent batches ----------------------
-        float qv = 0.f;
-        if (tid < H) qv = load_q_elem(a.q, a.q_dt, bh * H + tid);
+        const size_t q_idx = bh * H + (tid < H ? tid : 0);
+        const uint32_t q_word = load_q_word(a.q, a.q_dt, q_idx);
         const char* bk_base = static_cast<const char*>(a.B_K) + (size_t)h * R * H * BES;
         const char* bv_base = static_cast<const char*>(a.B_V) + (size_t)h * R * H * BES;
         u32x4 bk[NBT], bv[NBT];
@@ -225,10 +227,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const char* svb = I8 ? reinterpret_cast<const char*>(a.s_V + bh * a.L_cap + t0) : nullptr;
         const uint32_t lane_off = (uint32_t)min(j, G - 1) * 16u;
 
+        // int8 scales are kept as raw fp16 bits, one per 32-bit register:
+        // two halves packed into one register would need the loads to land
+        // before the next requests go out.
         u32x4 kA[U], vA[U], kB[U], vB[U];
-        uint16_t skA[U], svA[U], skB[U], svB[U];
+        uint32_t skA[U], svA[U], skB[U], svB[U];
 
-        auto load_tile = [&](int tb, u32x4* kr, u32x4* vr, uint16_t* sk, uint16_t* sv) {
+        auto load_tile = [&](int tb, u32x4* kr, u32x4* vr, uint32_t* sk, uint32_t* sv) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t row = (uint32_t)min(tb + u * RW + g, ntok - 1);
@@ -250,6 +255,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         if (tb + STEP < ntok) load_tile(tb + STEP, kB, vB, skB, svB);
 
         // ---- q' = (sigma log2 e) B_K q from the chunks in registers ------------
+        const float qv = q_word_value(q_word, a.q_dt, q_idx);
         if (tid < H) sh_q[tid] = qv;
         if (DENSE && tid < H) sh_qp[tid] = qv * a.scale_log2;
         __syncthreads();
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
 
-        auto consume = [&](int tbc, const u32x4* kr, const u32x4* vr, const uint16_t* sk, const uint16_t* sv) {
+        auto consume = [&](int tbc, const u32x4* kr, const u32x4* vr, const uint32_t* sk, const uint32_t* sv) {
             float sc[U];
             float mloc = kNegInf;
 #pragma unroll
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 float part = chunk_dot<CT>(kr[u], qp);
                 if constexpr (I8) part -= qoff;
                 float d = group_sum<GP>(part);
-                if constexpr (I8) d *= f16_to_f32(sk[u]);
+                if constexpr (I8) d *= f16_to_f32(uint16_t(sk[u]));
                 sc[u] = (tbc + u * RW + g) < ntok ? d : kNegInf;
                 mloc = fmaxf(mloc, sc[u]);
             }
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 l += p;
                 float w = p;
                 if constexpr (I8) {
-                    w *= f16_to_f32(sv[u]);
+                    w *= f16_to_f32(uint16_t(sv[u]));
                     pw += w;
                 }
                 chunk_axpy<CT>(vr[u], w, acc);
@@ -328,11 +334,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         // requests only tiles that exist, so nothing is left in flight.
         const int nt = (ntok > tb) ? (ntok - tb + STEP - 1) / STEP : 0;
         int k = 0;
+        // The scheduling barriers pin each refill between the two consumes:
+        // sunk below the second consume, the refill left that consume
+        // waiting for every load in flight (vmcnt(0)) instead of its own.
         for (; k + 3 < nt; k += 2) {
             consume(tb + k * STEP, kA, vA, skA, svA);
             load_tile(tb + (k + 2) * STEP, kA, vA, skA, svA);
+            __builtin_amdgcn_sched_barrier(0);
             consume(tb + (k + 1) * STEP, kB, vB, skB, svB);
             load_tile(tb + (k + 3) * STEP, kB, vB, skB, svB);
+            __builtin_amdgcn_sched_barrier(0);
         }
         const int rem = nt - k;
         if (rem >= 1) consume(tb + k * STEP, kA, vA, skA, svA);
