@@ -36,7 +36,12 @@ Readings where the pages are silent:
 * l = 0 gives a zero output;
 * int8 latents dequantise as code * fp16 scale of their (b, h, token) row;
 * an appended latent row is x . A_Kh computed exactly and rounded once to
-  the cache dtype (nearest, ties to even).
+  the cache dtype (nearest, ties to even);
+* an int8 cache row (8-bit storage of the pages' W8A8 setting) is stored
+  as symmetric absmax codes: scale = fp16(absmax / 127), code =
+  clamp(round_half_even(c / scale), -127, 127), a zero row has scale 0.
+  Where these decisions turn floats into integers they are taken in fp32,
+  the precision the GPU takes them in.
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by tests that do not reuse its own formula.
@@ -51,7 +56,8 @@ __all__ = [
     "upcast", "dequant_latent", "reconstruct", "softmax_weights", "attend",
     "split_bounds", "segment_attend", "combine", "decode_attn",
     "decode_attn_one", "decode_partials_one", "append_latents",
-    "apply_append", "round_to_bf16_bits",
+    "apply_append", "round_to_bf16_bits", "quantize_latent_rows",
+    "apply_append_int8",
 ]
 
 
@@ -266,3 +272,53 @@ def apply_append(inp):
             C_K[b, :, p, :] = round_to_bf16_bits(cK[b])
             C_V[b, :, p, :] = round_to_bf16_bits(cV[b])
     return C_K, C_V, cK, cV
+
+
+def quantize_latent_rows(c: np.ndarray):
+    """Symmetric absmax int8 storage of latent rows (last axis) -> (codes, scale bits).
+
+    The pages quantise activations and cached latents to 8 bits (W8A8;
+    German page section 3, Arabic page section 2d) without fixing the
+    quantiser; the reading here is the common symmetric per-row form:
+    scale = fp16(max |c| / 127), code = clamp(round_half_even(c / scale),
+    -127, 127), and a row whose scale is 0 stores zeros.  The decisions are
+    taken in fp32, as the kernel takes them: c is rounded to fp32 once,
+    max|c| / 127 and c / scale are single fp32 operations, and the scale is
+    rounded to fp16 (nearest, ties to even).  Scales are returned as
+    float16 values.
+
+    Parity: pinned by hand-worked rows (rounding, ties, clamp, zero row).
+    """
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(c32), axis=-1)
+    scale16 = np.divide(amax, np.float32(127.0), dtype=np.float32).astype(np.float16)
+    s32 = scale16.astype(np.float32)[..., None]
+    codes = np.zeros(c32.shape, dtype=np.float32)
+    ok = np.broadcast_to(s32 > 0, c32.shape)
+    ratio = np.divide(c32, np.where(s32 > 0, s32, np.float32(1.0)), dtype=np.float32)
+    codes[ok] = np.rint(ratio[ok])
+    codes = np.clip(codes, -127, 127).astype(np.int8)
+    return codes, scale16
+
+
+def apply_append_int8(inp):
+    """Int8 caches after appending x.A_Kh / x.A_Vh at row pos[b].
+
+    The latent is computed exactly (append_latents), then stored with
+    quantize_latent_rows.  Returns (C_K, C_V, s_K, s_V, latK_f64, latV_f64)
+    with codes int8 and scales float16; rows with pos outside [0, L_cap) are
+    not written.
+    """
+    if inp.C_dt != "i8":
+        raise ValueError("apply_append_int8 covers int8 caches")
+    cK = append_latents(inp.x, inp.x_dt, inp.A_K, inp.A_dt, inp.nh, inp.r)
+    cV = append_latents(inp.x, inp.x_dt, inp.A_V, inp.A_dt, inp.nh, inp.r)
+    C_K, C_V = inp.C_K.copy(), inp.C_V.copy()
+    s_K = np.asarray(inp.s_K, dtype=np.float16).copy()
+    s_V = np.asarray(inp.s_V, dtype=np.float16).copy()
+    for b in range(inp.nb):
+        p = int(inp.pos[b])
+        if 0 <= p < inp.L_cap:
+            C_K[b, :, p, :], s_K[b, :, p] = quantize_latent_rows(cK[b])
+            C_V[b, :, p, :], s_V[b, :, p] = quantize_latent_rows(cV[b])
+    return C_K, C_V, s_K, s_V, cK, cV

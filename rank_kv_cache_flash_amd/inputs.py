@@ -182,10 +182,13 @@ def make_decode_inputs(nb, nh, H, r, L, L_cap, *, seed, act_dt="bf16", C_dt="bf1
 
 
 def make_ragged_step_inputs(nb, nh, H, r, E, L_lo, L_hi, L_cap, *, seed, q_gain=1.0,
-                            dt="bf16") -> DecodeInputs:
-    """Full decode step: append x.A_Kh / x.A_Vh at pos = L-1, then attend L tokens."""
+                            dt="bf16", C_dt=None) -> DecodeInputs:
+    """Full decode step: append x.A_Kh / x.A_Vh at pos = L-1, then attend L tokens.
+
+    x, A, q and B are stored in `dt`; the caches in `C_dt` (default `dt`;
+    "i8" gives int8 codes with fp16 per-row scales)."""
     L = _rng(seed, T_L).integers(L_lo, L_hi, size=nb, endpoint=True).astype(np.int32)
-    inp = make_decode_inputs(nb, nh, H, r, L, L_cap, seed=seed, act_dt=dt, C_dt=dt,
+    inp = make_decode_inputs(nb, nh, H, r, L, L_cap, seed=seed, act_dt=dt, C_dt=C_dt or dt,
                              fill=L - 1, q_gain=q_gain)
     x = _normal(seed, (T_X,), (nb, E), 1.0 / np.sqrt(E))
     A_K = _normal(seed, (T_AK,), (E, nh * r), 1.0 / np.sqrt(r))

@@ -147,6 +147,38 @@ def _decode_one_short(inp, b, h, softmax_scale=None, *, C_K=None, C_V=None, _ori
     return _orig(j, b, h, softmax_scale, C_K=C_K, C_V=C_V)
 
 
+def _q8_floor(c):
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32)
+    s16 = (np.max(np.abs(c32), axis=-1) / np.float32(127)).astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    q = np.where(s32 > 0, np.floor(c32 / np.where(s32 > 0, s32, 1)), 0)
+    return np.clip(q, -127, 127).astype(np.int8), s16
+
+
+def _q8_no_fp16_scale(c):
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32)
+    s32 = (np.max(np.abs(c32), axis=-1) / np.float32(127))[..., None]
+    q = np.where(s32 > 0, np.rint(c32 / np.where(s32 > 0, s32, 1)), 0)
+    return np.clip(q, -127, 127).astype(np.int8), s32[..., 0].astype(np.float16)
+
+
+def _q8_clamp128(c):
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32)
+    s16 = (np.max(np.abs(c32), axis=-1) / np.float32(127)).astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    q = np.where(s32 > 0, np.rint(c32 / np.where(s32 > 0, s32, 1)), 0)
+    return np.clip(q, -128, 127).astype(np.int8), s16
+
+
+def _q8_half_away(c):
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32)
+    s16 = (np.max(np.abs(c32), axis=-1) / np.float32(127)).astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    r = c32 / np.where(s32 > 0, s32, 1)
+    q = np.where(s32 > 0, np.sign(r) * np.floor(np.abs(r) + 0.5), 0)
+    return np.clip(q, -127, 127).astype(np.int8), s16
+
+
 MUTANTS = {
     "softmax without max shift": ("softmax_weights", _softmax_nomax),
     "softmax sign flipped": ("softmax_weights", _softmax_sign),
@@ -165,6 +197,10 @@ MUTANTS = {
     "bf16 rounding truncates": ("round_to_bf16_bits", _round_truncate),
     "bf16 rounding ties away": ("round_to_bf16_bits", _round_half_up),
     "one token short": ("decode_attn_one", _decode_one_short),
+    "int8 code truncated": ("quantize_latent_rows", _q8_floor),
+    "int8 scale not rounded to fp16": ("quantize_latent_rows", _q8_no_fp16_scale),
+    "int8 clamp at -128": ("quantize_latent_rows", _q8_clamp128),
+    "int8 ties away from zero": ("quantize_latent_rows", _q8_half_away),
 }
 
 

@@ -349,3 +349,63 @@ def test_apply_append_writes_rounded_row_at_pos():
         back = O.upcast(CK[b, :, p], "bf16")
         ulp = np.ldexp(1.0, np.frexp(np.abs(cK[b]))[1] - 8)
         assert np.all(np.abs(back - cK[b]) <= ulp / 2 + 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# int8 latent rows (symmetric absmax, fp16 scale): hand-worked values
+# ---------------------------------------------------------------------------
+def test_int8_rows_hand_worked():
+    # absmax 1: 1/127 = 0.0078740... rounds to fp16 1032 * 2^-17; then
+    # 0.5 / s = 63.504 -> 64, 1 / s = 127.008 -> 127, 0.25 / s = 31.752 -> 32.
+    codes, scale = O.quantize_latent_rows(np.array([[0.5, -1.0, 0.25, 0.0]]))
+    assert float(scale[0]) == 1032 * 2.0 ** -17
+    assert codes.tolist() == [[64, -127, 32, 0]]
+    assert codes.dtype == np.int8 and scale.dtype == np.float16
+
+
+def test_int8_rows_ties_go_to_even():
+    # absmax 127 * 2^-7 makes the scale exactly 2^-7: ratios 2.5 and 3.5 and -0.5 are ties.
+    s = 2.0 ** -7
+    codes, scale = O.quantize_latent_rows(np.array([[127 * s, 2.5 * s, 3.5 * s, -0.5 * s, -1.5 * s]]))
+    assert float(scale[0]) == s
+    assert codes.tolist() == [[127, 2, 4, 0, -2]]
+
+
+def test_int8_rows_zero_row_and_clamp():
+    # zero row: scale 0, codes 0
+    codes, scale = O.quantize_latent_rows(np.zeros((2, 3)))
+    assert np.all(scale == 0) and np.all(codes == 0)
+    # absmax / 127 = 1.4 * 2^-24 rounds down to the smallest fp16 subnormal 2^-24,
+    # so the largest entries sit at 177.8 scales: they clamp to +-127, 2^-24 itself is code 1.
+    t = 2.0 ** -24
+    codes, scale = O.quantize_latent_rows(np.array([[127 * 1.4 * t, -127 * 1.4 * t, 0.0, t]]))
+    assert float(scale[0]) == t
+    assert codes.tolist() == [[127, -127, 0, 1]]
+
+
+def test_int8_rows_error_bound():
+    # Away from the clamp, code * scale is within half a scale of the value (plus fp32 rounding).
+    c = RNG.standard_normal((50, 48)) * np.exp(RNG.uniform(-8, 4, (50, 1)))
+    codes, scale = O.quantize_latent_rows(c)
+    s = scale.astype(np.float64)[:, None]
+    err = np.abs(codes * s - c)
+    assert np.all(err <= 0.5 * s * (1 + 1e-6) + np.abs(c) * 2.0 ** -23)
+    assert np.all(np.abs(codes).max(axis=1) == 127)      # the absmax entry maps to +-127
+
+
+def test_apply_append_int8_writes_codes_and_scales_at_pos():
+    from rank_kv_cache_flash_amd import inputs as I
+    inp = I.make_ragged_step_inputs(3, 2, 64, 16, 256, 3, 9, 9, seed=8, C_dt="i8")
+    inp.pos[2] = 9                                       # out of range: row left alone
+    CK, CV, sK, sV, cK, cV = O.apply_append_int8(inp)
+    for b in range(2):
+        p = int(inp.pos[b])
+        for h in range(2):
+            deq = CK[b, h, p].astype(np.float64) * float(sK[b, h, p])
+            assert np.all(np.abs(deq - cK[b, h]) <= 0.5 * float(sK[b, h, p]) * (1 + 1e-6) + 1e-12)
+            assert np.abs(CV[b, h, p]).max() == 127
+        # every other row untouched
+        keep = np.ones(inp.L_cap, bool); keep[p] = False
+        assert np.array_equal(CK[b][:, keep], inp.C_K[b][:, keep])
+        assert np.array_equal(sK[b][:, keep], np.asarray(inp.s_K[b])[:, keep])
+    assert np.array_equal(CK[2], inp.C_K[2]) and np.array_equal(sV[2], np.asarray(inp.s_V[2]))
