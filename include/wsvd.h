@@ -157,8 +157,16 @@ int wsvd_combine_splits(int nb, int nh, int H, int n_splits,
  *     C_V[b, h, pos[b], :] = x[b, :] A_V[:, h*r:(h+1)*r]
  *
  * accumulated in fp32 on matrix cores and rounded once to C_dt (nearest,
- * ties to even).  Only C_dt == WSVD_BF16 or WSVD_F32 caches are written by
- * this version (WSVD_I8 returns WSVD_ERR_UNSUPPORTED).
+ * ties to even).
+ *
+ * Int8 caches (the 8-bit latent storage of the pages' W8A8 setting, German
+ * page section 3, Arabic page section 2d) store each new (b, h) row as
+ * symmetric absmax codes: scale = fp16(max_i |c_i| / 127) goes to
+ * s_K / s_V[b, h, pos[b]], code_i = clamp(round_half_even(c_i / scale),
+ * -127, 127); a row whose scale is 0 stores zeros.  The decode reads such
+ * rows as code * scale.  Int8 caches need r in {16, 32, 64} (a head must be
+ * whole 16-column groups of one 64-column tile; r = 48 returns
+ * WSVD_ERR_UNSUPPORTED).
  *
  *   nb, E, nh, r     batch, embedding width, heads, rank (r as above)
  *   L_cap            cache capacity in tokens
@@ -166,8 +174,9 @@ int wsvd_combine_splits(int nb, int nh, int H, int n_splits,
  *   A_K, A_V, A_dt   [E, nh*r]       BF16 (column block h is A_Kh)
  *   pos              int32 [nb] device: row to write; rows with pos[b]
  *                    outside [0, L_cap) are skipped
- *   C_K, C_V, C_dt   [nb, nh, L_cap, r]
- *   s_K, s_V         unused (must be NULL) for BF16/F32 caches
+ *   C_K, C_V, C_dt   [nb, nh, L_cap, r]   BF16 | F32 | I8
+ *   s_K, s_V         fp16 [nb, nh, L_cap] row scales, required (16-byte
+ *                    aligned) iff C_dt == WSVD_I8; must be NULL otherwise
  *   workspace        device scratch of wsvd_append_workspace_bytes(...)
  *                    bytes, 256-byte aligned: fp32 split-E partial tiles
  *                    and one arrival counter per output tile.  It must be

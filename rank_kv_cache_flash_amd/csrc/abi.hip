@@ -209,8 +209,13 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     if (!x || !A_K || !A_V || !pos || !C_K || !C_V) return WSVD_ERR_NULL;
     if (x_dt != WSVD_BF16 || A_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
     if (!cache_dtype_ok(C_dt)) return WSVD_ERR_DTYPE;
-    if (C_dt == WSVD_I8) return WSVD_ERR_UNSUPPORTED;
-    if (s_K || s_V) return WSVD_ERR_SHAPE;
+    if (C_dt == WSVD_I8) {
+        if (!s_K || !s_V) return WSVD_ERR_NULL;
+        if (!aligned16(s_K) || !aligned16(s_V)) return WSVD_ERR_ALIGN;
+        if (r == 48) return WSVD_ERR_UNSUPPORTED;  // a head must be whole 16-column groups of one 64-column tile
+    } else if (s_K || s_V) {
+        return WSVD_ERR_SHAPE;
+    }
     if (!rank_ok(r) || E % 256 != 0) return WSVD_ERR_UNSUPPORTED;
     if ((long long)nb * nh * L_cap * r > (1ll << 46) || (long long)E * nh * r > (1ll << 40)) return WSVD_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(A_K) || !aligned16(A_V) || !aligned16(pos) || !aligned16(C_K) ||
@@ -232,6 +237,8 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     a.C_K = C_K;
     a.C_V = C_V;
     a.C_dt = C_dt;
+    a.s_K = s_K;
+    a.s_V = s_V;
     a.KS = wsvd::append_num_esplits(nb, E, nh, r);
     const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
     a.part = need > 0 ? static_cast<float*>(workspace) : nullptr;

@@ -140,6 +140,49 @@ __device__ __forceinline__ void mma_stage(const Stage& s, uint16_t* sB, uint16_t
 }
 
 
+// int8 cache rows (r in 16, 32, 64, so a head's r columns are whole
+// 16-column groups of one tile): per (row, head) the absmax over the head's
+// columns -- 16 lanes by DPP, then the head's column groups in registers --
+// gives the fp16 scale fp16(absmax / 127); codes are
+// clamp(round_half_even(v / scale), -127, 127), a zero row stores scale 0.
+// Rows m0r .. m0r + 3 of this lane, columns n0 + jn * 16 + (lane & 15).
+__device__ __forceinline__ void store_int8_rows(const AppendArgs& a, const f32x4 (&acc)[4], void* C, uint16_t* S,
+                                                const int (&prow)[4], int n0, int m0r, int lane) {
+    const int N1 = a.nh * a.r;
+    const int gj = a.r >> 4;  // column groups per head: 1, 2 or 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float mx[4];
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) mx[jn] = group_max<16>(fabsf(acc[jn][i]));
+        // combine the groups of each head (heads start at a multiple of gj)
+        if (gj >= 2) {
+            const float m01 = fmaxf(mx[0], mx[1]), m23 = fmaxf(mx[2], mx[3]);
+            mx[0] = mx[1] = m01;
+            mx[2] = mx[3] = m23;
+        }
+        if (gj == 4) mx[0] = mx[1] = mx[2] = mx[3] = fmaxf(mx[0], mx[2]);
+        const int m = m0r + i;
+        const int p = prow[i];
+        if (m >= a.nb || p < 0 || p >= a.L_cap) continue;
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const int n = n0 + jn * 16 + (lane & 15);
+            if (n >= N1) continue;
+            const int h = n / a.r;
+            const int col = n - h * a.r;
+            const uint16_t sb = f32_to_f16(mx[jn] / 127.f);
+            const float sc = f16_to_f32(sb);
+            float code = 0.f;
+            if (sc > 0.f) code = fminf(fmaxf(__builtin_rintf(acc[jn][i] / sc), -127.f), 127.f);
+            const size_t row = ((size_t)m * a.nh + h) * a.L_cap + p;
+            __builtin_nontemporal_store((int8_t)(int)code, static_cast<int8_t*>(C) + row * a.r + col);
+            if (col == 0)
+                __hip_atomic_store(S + row, sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sB[AP_NT * AP_PITCH];
     __shared__ __attribute__((aligned(16))) uint16_t sX[AP_MT * AP_PITCH];
@@ -245,8 +288,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         load_pos();
     }
 
-    // Round once and scatter into the caches.
     void* C = kv ? a.C_V : a.C_K;
+    if (a.C_dt == WSVD_I8) {
+        store_int8_rows(a, acc, C, kv ? a.s_V : a.s_K, prow, n0, m0 + wave * 16 + (lane >> 4) * 4, lane);
+        return;
+    }
+    // Round once and scatter into the caches.
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
         const int n = n0 + jn * 16 + (lane & 15);

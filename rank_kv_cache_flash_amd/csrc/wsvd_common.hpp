@@ -90,6 +90,16 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Maximum over aligned groups of N lanes, like group_sum.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (N >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return v;
+}
+
 // Lane l combined with lane l^16 (l^32): gfx950 permlane swaps exchange rows
 // of two registers; with both operands equal, the two results hold v_l and
 // v_(l^16) (v_(l^32)) in every lane.  VALU only, no LDS round trip.

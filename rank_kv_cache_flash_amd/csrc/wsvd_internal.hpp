@@ -46,6 +46,8 @@ struct AppendArgs {
     void* C_K;
     void* C_V;
     int C_dt;
+    uint16_t* s_K;        // fp16 [nb, nh, L_cap] row scales (int8 caches only)
+    uint16_t* s_V;
     float* part;          // fp32 split-E partial tiles (KS > 1 only)
     unsigned* counters;   // per-tile arrival counters, zero between calls
     int KS;               // number of E splits

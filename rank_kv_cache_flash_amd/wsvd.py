@@ -216,20 +216,20 @@ def combine_splits(o_part, lse_part, *, out=None, out_dtype=torch.float32, strea
     return out
 
 
-def append_latent(x, A_K, A_V, pos, C_K, C_V, *, workspace=None, stream=None):
+def append_latent(x, A_K, A_V, pos, C_K, C_V, *, s_K=None, s_V=None, workspace=None, stream=None):
     """wsvd_append_latent: x [nb, E] bf16, A_K / A_V [E, nh*r] bf16, pos int32 [nb],
-    caches [nb, nh, L_cap, r] written in place at row pos[b]."""
+    caches [nb, nh, L_cap, r] (bf16 / f32, or int8 with fp16 row scales
+    s_K / s_V [nb, nh, L_cap]) written in place at row pos[b]."""
     for t, n in ((x, "x"), (A_K, "A_K"), (A_V, "A_V"), (pos, "pos"), (C_K, "C_K"), (C_V, "C_V"),
-                 (workspace, "workspace")):
+                 (s_K, "s_K"), (s_V, "s_V"), (workspace, "workspace")):
         _dev(t, n)
     nb, E = x.shape
     _, nh, L_cap, r = C_K.shape
-    need = append_workspace_bytes(nb, E, nh, r)
     if workspace is None:
         workspace = append_workspace(nb, E, nh, r, device=x.device)
     st = lib().wsvd_append_latent(nb, E, nh, r, L_cap, _ptr(x), _DT[x.dtype], _ptr(A_K), _ptr(A_V), _DT[A_K.dtype],
-                                  _ptr(pos), _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], None, None, _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream))
+                                  _ptr(pos), _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], _ptr(s_K), _ptr(s_V),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "wsvd_append_latent")
     return C_K, C_V
 
@@ -309,15 +309,15 @@ class PreparedDecode:
 class PreparedAppend:
     """wsvd_append_latent with fixed buffers; __call__(stream) enqueues it."""
 
-    def __init__(self, x, A_K, A_V, pos, C_K, C_V, *, workspace):
+    def __init__(self, x, A_K, A_V, pos, C_K, C_V, *, workspace, s_K=None, s_V=None):
         for t, n in ((x, "x"), (A_K, "A_K"), (A_V, "A_V"), (pos, "pos"), (C_K, "C_K"), (C_V, "C_V"),
-                     (workspace, "workspace")):
+                     (s_K, "s_K"), (s_V, "s_V"), (workspace, "workspace")):
             _dev(t, n)
         nb, E = x.shape
         _, nh, L_cap, r = C_K.shape
-        self._keep = (x, A_K, A_V, pos, C_K, C_V, workspace)
+        self._keep = (x, A_K, A_V, pos, C_K, C_V, s_K, s_V, workspace)
         self._args = (nb, E, nh, r, L_cap, _ptr(x), _DT[x.dtype], _ptr(A_K), _ptr(A_V), _DT[A_K.dtype], _ptr(pos),
-                      _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], None, None, _ptr(workspace),
+                      _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], _ptr(s_K), _ptr(s_V), _ptr(workspace),
                       workspace.numel() * workspace.element_size())
         self._fn = lib().wsvd_append_latent
 

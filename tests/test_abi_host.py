@@ -130,7 +130,9 @@ def append(L, **kw):
     (dict(nb=0), ESHAPE), (dict(E=-4), ESHAPE), (dict(L_cap=0), ESHAPE),
     (dict(x=None), ENULL), (dict(A_V=None), ENULL), (dict(pos=None), ENULL), (dict(C_K=None), ENULL),
     (dict(x_dt=F32), EDTYPE), (dict(A_dt=F16), EDTYPE), (dict(C_dt=F16), EDTYPE),
-    (dict(C_dt=I8), EUNSUP), (dict(r=40), EUNSUP), (dict(E=4000), EUNSUP),
+    (dict(C_dt=I8), ENULL), (dict(C_dt=I8, s_K=P), ENULL), (dict(C_dt=I8, s_K=P, s_V=P), EUNSUP),
+    (dict(C_dt=I8, s_K=P, s_V=P + 2, r=32), EALIGN), (dict(C_dt=I8, s_K=P, s_V=P, r=32), EWS),
+    (dict(r=40), EUNSUP), (dict(E=4000), EUNSUP),
     (dict(s_K=P), ESHAPE),
     (dict(x=P + 2), EALIGN), (dict(A_K=P + 8), EALIGN), (dict(C_V=P + 4), EALIGN),
     (dict(ws=None), EWS), (dict(ws_bytes=100), EWS),

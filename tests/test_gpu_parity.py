@@ -312,6 +312,90 @@ def test_append_row_tiles_and_reuse(W):
         assert appended_row_ok(gV[b, :, p], cV[b], inp2.x[b:b + 1], inp2.A_V, inp2.nh, inp2.r).all()
 
 
+# ---------------------------------------------------------------------------
+# append into int8 caches (absmax rows, fp16 scales)
+# ---------------------------------------------------------------------------
+def int8_rows_check(codes, scales, exact, x, A, nh, r, what):
+    """GPU int8 rows vs the oracle's quantiser on the exact latent.
+
+    The GPU rounds its own fp32 dot (length E), so near a rounding boundary
+    its decision may fall on the other side of the oracle's; the bound on
+    that is the fp32 accumulation bound E 2^-24 sum_e |x_e A_e|.  Checked:
+    scales within one fp16 ulp of the oracle's, every code within half a
+    scale (plus that bound) of the exact value, codes within 1 of the
+    oracle's and equal to them almost everywhere."""
+    ref_codes, ref_scales = O.quantize_latent_rows(exact)
+    xx, AA = O.upcast(x, "bf16"), O.upcast(A, "bf16")
+    bound = xx.shape[1] * 2.0 ** -24 * (np.abs(xx) @ np.abs(AA)).reshape(exact.shape)
+    sg = np.asarray(scales, np.float16).astype(np.float64)
+    sr = ref_scales.astype(np.float64)
+    ulp = np.spacing(ref_scales.astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(sg - sr) <= ulp), f"{what}: scale off by more than one fp16 ulp"
+    deq = codes.astype(np.float64) * sg[..., None]
+    assert np.all(np.abs(deq - exact) <= 0.5 * sg[..., None] * (1 + 1e-6) + bound + 1e-30), f"{what}: code error"
+    d = np.abs(codes.astype(np.int32) - ref_codes.astype(np.int32))
+    assert d.max() <= 1, f"{what}: code differs by {d.max()}"
+    assert np.mean(d == 0) >= 0.99, f"{what}: only {np.mean(d == 0):.4f} of codes equal"
+    return float(np.mean(d == 0))
+
+
+def _append_int8_case(W, inp, workspace=None):
+    d = W.device_inputs(inp)
+    W.append_latent(d["x"], d["A_K"], d["A_V"], d["pos"], d["C_K"], d["C_V"], s_K=d["s_K"], s_V=d["s_V"],
+                    workspace=workspace)
+    torch.cuda.synchronize()
+    CK, CV, sK, sV, cK, cV = O.apply_append_int8(inp)
+    gK, gV = d["C_K"].cpu().numpy(), d["C_V"].cpu().numpy()
+    hK = d["s_K"].cpu().numpy().astype(np.float16)
+    hV = d["s_V"].cpu().numpy().astype(np.float16)
+    eq = []
+    rows = [b for b in range(inp.nb) if 0 <= int(inp.pos[b]) < inp.L_cap]
+    for lat, g, hs, A, tag in ((cK, gK, hK, inp.A_K, "K"), (cV, gV, hV, inp.A_V, "V")):
+        gc = np.stack([g[b, :, int(inp.pos[b])] for b in rows])
+        gs = np.stack([hs[b, :, int(inp.pos[b])] for b in rows])
+        eq.append(int8_rows_check(gc, gs, lat[rows], inp.x[rows], A, inp.nh, inp.r, f"int8 append {tag}"))
+    # untouched rows stay untouched
+    mask = np.ones(gK.shape[:3], bool)
+    for b in rows:
+        mask[b, :, int(inp.pos[b])] = False
+    assert np.array_equal(gK[mask], inp.C_K[mask]) and np.array_equal(gV[mask], inp.C_V[mask])
+    assert np.array_equal(hK[mask], np.asarray(inp.s_K)[mask]) and np.array_equal(hV[mask], np.asarray(inp.s_V)[mask])
+    print(f"[parity] int8 append nb={inp.nb} r={inp.r} E={inp.E}: codes equal to the oracle's: {min(eq):.5f}",
+          flush=True)
+    return d, CK, CV, sK, sV
+
+
+def test_append_int8_small(W):
+    inp = I.make_ragged_step_inputs(5, 4, 128, 32, 512, 3, 40, 40, seed=41, C_dt="i8")
+    inp.pos[3] = 40      # out of range: skipped
+    inp.pos[4] = -1
+    _append_int8_case(W, inp)
+
+
+@pytest.mark.parametrize("r,E,nb", [(16, 768, 7), (32, 2048, 70), (64, 1024, 9)])
+def test_append_int8_ranks(W, r, E, nb):
+    inp = I.make_ragged_step_inputs(nb, 4, 128, r, E, 2, 20, 20, seed=50 + r, C_dt="i8")
+    _append_int8_case(W, inp)
+
+
+def test_append_int8_then_decode(W):
+    """The int8-cache workload's shapes end to end: the new token's latents are
+    quantised on the GPU into int8 rows, then the fused decode attends over
+    the cache; the oracle does both steps itself."""
+    inp = I.make_ragged_step_inputs(32, 32, 128, 32, 4096, 1024, 2048, 2048, seed=404, C_dt="i8")
+    d, CK, CV, sK, sV = _append_int8_case(W, inp)
+    out, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], s_K=d["s_K"], s_V=d["s_V"])
+    torch.cuda.synchronize()
+    g = f64(out)
+    import copy
+    ref_inp = copy.copy(inp)
+    ref_inp.s_K, ref_inp.s_V = sK, sV
+    pairs = sampled_pairs(inp.nb, inp.nh, 40, 9)
+    ref = O.decode_attn(ref_inp, C_K=CK, C_V=CV, pairs=pairs)
+    check("int8 append + decode sampled", np.stack([g[b, h] for b, h in pairs]), np.stack([ref[p] for p in pairs]),
+          TOL["i8"])
+
+
 def test_config5_full_step(W):
     c = CONFIGS[5]
     inp = c.make()
