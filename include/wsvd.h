@@ -160,7 +160,7 @@ int wsvd_combine_splits(int nb, int nh, int H, int n_splits,
  * ties to even).
  *
  * Int8 caches (the 8-bit latent storage of the pages' W8A8 setting, German
- * page section 3, Arabic page section 2d) store each new (b, h) row as
+ * page section 2C, Arabic page section 2c) store each new (b, h) row as
  * symmetric absmax codes: scale = fp16(max_i |c_i| / 127) goes to
  * s_K / s_V[b, h, pos[b]], code_i = clamp(round_half_even(c_i / scale),
  * -127, 127); a row whose scale is 0 stores zeros.  The decode reads such

@@ -4,4 +4,8 @@ Test infrastructure: imported only by the tests, the package smoke check
 and the benchmark's CPU-baseline leg.  Never part of the GPU path.
 """
 from .wsvd_oracle import *  # noqa: F401,F403
-from .wsvd_oracle import __all__  # noqa: F401
+from .wsvd_oracle import __all__ as _core_all
+from .w8a8 import *  # noqa: F401,F403
+from .w8a8 import __all__ as _w8a8_all
+
+__all__ = list(_core_all) + list(_w8a8_all)

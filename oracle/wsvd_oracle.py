@@ -275,10 +275,10 @@ def apply_append(inp):
 
 
 def quantize_latent_rows(c: np.ndarray):
-    """Symmetric absmax int8 storage of latent rows (last axis) -> (codes, scale bits).
+    """Symmetric absmax int8 storage of latent rows (last axis) -> (codes, scales).
 
     The pages quantise activations and cached latents to 8 bits (W8A8;
-    German page section 3, Arabic page section 2d) without fixing the
+    German page section 2C, Arabic page section 2c) without fixing the
     quantiser; the reading here is the common symmetric per-row form:
     scale = fp16(max |c| / 127), code = clamp(round_half_even(c / scale),
     -127, 127), and a row whose scale is 0 stores zeros.  The decisions are

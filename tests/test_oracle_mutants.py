@@ -179,6 +179,28 @@ def _q8_half_away(c):
     return np.clip(q, -127, 127).astype(np.int8), s16
 
 
+def _hadamard_no_minus(n):
+    return np.ones((n, n), dtype=np.int64)
+
+
+def _rotate_unnormalised(x, x_dt):
+    xx = W.upcast(x, x_dt)
+    return xx @ oracle.w8a8.hadamard_matrix(xx.shape[-1]).astype(np.float64)
+
+
+def _w8a8_drop_weight_scale(xq, sx, AqT, sA, nh, r):
+    acc = np.asarray(xq, np.int64) @ np.asarray(AqT, np.int64).T
+    return (acc * np.asarray(sx, np.float64)[:, None]).reshape(acc.shape[0], nh, r)
+
+
+def _qrows_f32_floor(v):
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    scale = (np.max(np.abs(v32), axis=-1) / np.float32(127)).astype(np.float32)
+    s = scale[..., None]
+    q = np.where(s > 0, np.floor(v32 / np.where(s > 0, s, 1)), 0)
+    return np.clip(q, -127, 127).astype(np.int8), scale
+
+
 MUTANTS = {
     "softmax without max shift": ("softmax_weights", _softmax_nomax),
     "softmax sign flipped": ("softmax_weights", _softmax_sign),
@@ -201,14 +223,20 @@ MUTANTS = {
     "int8 scale not rounded to fp16": ("quantize_latent_rows", _q8_no_fp16_scale),
     "int8 clamp at -128": ("quantize_latent_rows", _q8_clamp128),
     "int8 ties away from zero": ("quantize_latent_rows", _q8_half_away),
+    "hadamard without the minus block": ("hadamard_matrix", _hadamard_no_minus),
+    "rotation not normalised": ("rotate_rows", _rotate_unnormalised),
+    "w8a8 weight scale dropped": ("w8a8_latents", _w8a8_drop_weight_scale),
+    "fp32-scale codes truncated": ("quantize_rows_f32", _qrows_f32_floor),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    monkeypatch.setattr(W, attr, fn)
-    monkeypatch.setattr(oracle, attr, fn)
+    import oracle.w8a8 as W8
+    for mod in (W, W8, oracle):
+        if hasattr(mod, attr):
+            monkeypatch.setattr(mod, attr, fn)
     caught = []
     for pname, pin, kw in PINS:
         try:

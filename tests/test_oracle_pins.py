@@ -409,3 +409,74 @@ def test_apply_append_int8_writes_codes_and_scales_at_pos():
         assert np.array_equal(CK[b][:, keep], inp.C_K[b][:, keep])
         assert np.array_equal(sK[b][:, keep], np.asarray(inp.s_K[b])[:, keep])
     assert np.array_equal(CK[2], inp.C_K[2]) and np.array_equal(sV[2], np.asarray(inp.s_V[2]))
+
+
+# ---------------------------------------------------------------------------
+# W8A8 projection: Hadamard rotation, per-row fp32-scale codes, integer product
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 64])
+def test_hadamard_matrix_is_sylvester(n):
+    h = O.hadamard_matrix(n)
+    assert np.array_equal(h, scipy.linalg.hadamard(n))
+    assert np.array_equal(h @ h.T, n * np.eye(n, dtype=np.int64))
+
+
+def test_rotation_hand_worked_and_orthogonal():
+    # H_4 = [[1,1,1,1],[1,-1,1,-1],[1,1,-1,-1],[1,-1,-1,1]]; [1,2,3,4] H_4 = [10,-2,-4,0]; / sqrt(4)
+    assert np.allclose(O.rotate_rows(np.array([[1.0, 2.0, 3.0, 4.0]]), "f64"), [[5.0, -1.0, -2.0, 0.0]], atol=0)
+    x = RNG.standard_normal((3, 256))
+    xr = O.rotate_rows(x, "f64")
+    assert np.allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    assert np.allclose(O.rotate_rows(xr, "f64"), x, atol=1e-12)       # H_E / sqrt(E) squares to I
+
+
+def test_quantize_rows_f32_hand_worked():
+    # scale fp32(1/127); 0.5 / scale rounds to 63.5 in fp32 and the tie goes to 64;
+    # 1 / scale = 127.0000005 -> 127; 0.25 / scale -> 31.75 -> 32.
+    codes, scale = O.quantize_rows_f32(np.array([[0.5, -1.0, 0.25, 0.0]]))
+    assert scale.dtype == np.float32 and scale[0] == np.float32(1.0) / np.float32(127.0)
+    assert codes.tolist() == [[64, -127, 32, 0]]
+    s = 2.0 ** -7                                   # exact scale: 2.5, 3.5, -0.5, -1.5 are ties
+    codes, scale = O.quantize_rows_f32(np.array([[127 * s, 2.5 * s, 3.5 * s, -0.5 * s, -1.5 * s]]))
+    assert scale[0] == s and codes.tolist() == [[127, 2, 4, 0, -2]]
+    codes, scale = O.quantize_rows_f32(np.zeros((1, 5)))
+    assert scale[0] == 0 and not codes.any()
+
+
+def test_prepare_factor_of_identity():
+    # A = I_4: A' = H_4 / 2, every column is +-1/2, so scale 1/254 and codes 127 * sign pattern of H_4.
+    AqT, sA = O.prepare_factor(np.eye(4), "f64")
+    assert np.array_equal(AqT.astype(np.int64), 127 * scipy.linalg.hadamard(4).T)
+    assert np.all(sA == np.float32(0.5) / np.float32(127.0))
+
+
+def test_w8a8_latents_brute_force():
+    xq = RNG.integers(-127, 128, (3, 8)).astype(np.int8)
+    AqT = RNG.integers(-127, 128, (6, 8)).astype(np.int8)
+    sx = np.array([0.5, 0.25, 2.0], np.float32)
+    sA = np.linspace(0.1, 0.6, 6).astype(np.float32)
+    got = O.w8a8_latents(xq, sx, AqT, sA, nh=2, r=3)
+    for b in range(3):
+        for n in range(6):
+            acc = sum(int(xq[b, e]) * int(AqT[n, e]) for e in range(8))
+            assert got[b, n // 3, n % 3] == acc * float(sx[b]) * float(sA[n])
+
+
+def test_w8a8_exact_case_and_error_bound():
+    # x = 1/2 everywhere rotates to (1, 0, 0, 0): codes exact; with A = I the pipeline returns x.
+    xq, sx = O.quantize_activations(np.full((1, 4), 0.5), "f64")
+    assert xq.tolist() == [[127, 0, 0, 0]]
+    AqT, sA = O.prepare_factor(np.eye(4), "f64")
+    c = O.w8a8_latents(xq, sx, AqT, sA, nh=1, r=4)
+    assert np.allclose(c.reshape(1, 4), 0.5, rtol=1e-7)
+    # random data: |w8a8 - x.A| within the two half-step quantisation errors
+    E, N = 256, 24
+    x = RNG.standard_normal((4, E)) / 16
+    A = RNG.standard_normal((E, N)) / 4
+    xq, sx = O.quantize_activations(x, "f64")
+    AqT, sA = O.prepare_factor(A, "f64")
+    c = O.w8a8_latents(xq, sx, AqT, sA, nh=2, r=12).reshape(4, N)
+    xr = O.rotate_rows(x, "f64")
+    Ar = (scipy.linalg.hadamard(E) @ A) / np.sqrt(E)
+    bound = (sx[:, None] / 2) @ np.abs(Ar).sum(0)[None, :] + np.abs(xr).sum(1)[:, None] * (sA[None, :] / 2) * (1 + 1e-6)
+    assert np.all(np.abs(c - x @ A) <= bound * 1.01 + 1e-12)
