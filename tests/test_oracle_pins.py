@@ -384,13 +384,16 @@ def test_int8_rows_zero_row_and_clamp():
 
 
 def test_int8_rows_error_bound():
-    # Away from the clamp, code * scale is within half a scale of the value (plus fp32 rounding).
-    c = RNG.standard_normal((50, 48)) * np.exp(RNG.uniform(-8, 4, (50, 1)))
+    # With normal (not subnormal) fp16 scales, code * scale is within half a scale of the
+    # value (plus fp32 rounding) and the absmax entry maps to +-127.
+    rng = np.random.default_rng(7)
+    c = rng.standard_normal((50, 48)) * np.exp(rng.uniform(-4, 4, (50, 1)))
     codes, scale = O.quantize_latent_rows(c)
     s = scale.astype(np.float64)[:, None]
     err = np.abs(codes * s - c)
     assert np.all(err <= 0.5 * s * (1 + 1e-6) + np.abs(c) * 2.0 ** -23)
-    assert np.all(np.abs(codes).max(axis=1) == 127)      # the absmax entry maps to +-127
+    assert np.all(scale >= np.float16(2.0 ** -14))
+    assert np.all(np.abs(codes).max(axis=1) == 127)
 
 
 def test_apply_append_int8_writes_codes_and_scales_at_pos():
