@@ -197,6 +197,56 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap,
                        hipStream_t stream);
 
 /*
+ * W8A8 projection of the new token (German page section 2C, Italian page
+ * section 2C, Japanese page section 2.3, Arabic page section 2c: the
+ * low-rank layers run with 8-bit weights and activations, and an
+ * orthogonal Hadamard rotation S1 smooths activation outliers before
+ * quantisation).  Readings: S1 = H_E / sqrt(E), the Sylvester Walsh-Hadamard
+ * matrix of order E (a power of two), which is symmetric and orthogonal, so
+ * x A = (x S1)(S1 A) and the factor side is rotated once, offline; codes are
+ * symmetric absmax int8 with one fp32 scale per row (token) or per column
+ * (factor output): s = max|v| / 127, code = clamp(round_half_even(v / s),
+ * -127, 127), zero codes when s == 0.  Supported E: powers of two from 256
+ * to 8192.
+ *
+ * wsvd_w8a8_prepare_factor -- offline: rotate a factor A [E, N] (F32 | BF16
+ * | F16, column block h of width r is A_Kh) down its columns and quantise
+ * each column: AqT int8 [N, E] (row n holds column n's codes, k-contiguous)
+ * and sA fp32 [N].
+ */
+int wsvd_w8a8_prepare_factor(int E, int N, const void* A, wsvd_dtype A_dt,
+                             int8_t* AqT, float* sA, hipStream_t stream);
+
+/*
+ * wsvd_w8a8_quantize_activations -- per step: rotate each token x[b, :]
+ * (F32 | BF16 | F16, [nb, E]) by S1 and quantise it: xq int8 [nb, E],
+ * sx fp32 [nb].
+ */
+int wsvd_w8a8_quantize_activations(int nb, int E, const void* x, wsvd_dtype x_dt,
+                                   int8_t* xq, float* sx, hipStream_t stream);
+
+/*
+ * wsvd_append_latent_w8a8 -- wsvd_append_latent with integer operands:
+ *
+ *     c[b, h*r + i] = (sum_e xq[b, e] AqT_K[h*r + i, e]) * sx[b] * sA_K[h*r + i]
+ *
+ * (the sum is exact: int32 on matrix cores), then c is stored in row pos[b]
+ * of C_K exactly as wsvd_append_latent stores it (BF16 | F32 rounded once;
+ * I8 as absmax codes with fp16 s_K); the same for V.  E must be a multiple
+ * of 512.  Workspace: wsvd_append_workspace_bytes(nb, E, nh, r), with the
+ * same zero-counter rule.  Other arguments as for wsvd_append_latent.
+ */
+int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap,
+                            const int8_t* xq, const float* sx,
+                            const int8_t* AqT_K, const int8_t* AqT_V,
+                            const float* sA_K, const float* sA_V,
+                            const int32_t* pos,
+                            void* C_K, void* C_V, wsvd_dtype C_dt,
+                            uint16_t* s_K, uint16_t* s_V,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * wsvd_dense_decode_attn -- the speed baseline the pages compare WSVD with:
  * ordinary Flash-Decoding attention over full K and V (Japanese page
  * section 4, German page section 4: decode latency against Flash Decoding).

@@ -202,12 +202,35 @@ int wsvd_combine_splits(int nb, int nh, int H, int n_splits, const float* o_part
                : WSVD_ERR_HIP;
 }
 
-int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, wsvd_dtype x_dt, const void* A_K,
-                       const void* A_V, wsvd_dtype A_dt, const int32_t* pos, void* C_K, void* C_V, wsvd_dtype C_dt,
-                       uint16_t* s_K, uint16_t* s_V, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0 || L_cap <= 0) return WSVD_ERR_SHAPE;
-    if (!x || !A_K || !A_V || !pos || !C_K || !C_V) return WSVD_ERR_NULL;
-    if (x_dt != WSVD_BF16 || A_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
+static bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int wsvd_w8a8_quantize_activations(int nb, int E, const void* x, wsvd_dtype x_dt, int8_t* xq, float* sx,
+                                   hipStream_t stream) {
+    if (nb <= 0 || E <= 0) return WSVD_ERR_SHAPE;
+    if (!x || !xq || !sx) return WSVD_ERR_NULL;
+    if (!act_dtype_ok(x_dt)) return WSVD_ERR_DTYPE;
+    if (!pow2_in(E, 256, 8192)) return WSVD_ERR_UNSUPPORTED;
+    if ((long long)nb * E > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return WSVD_ERR_ALIGN;
+    return wsvd::launch_w8a8_quantize_rows(nb, E, x, x_dt, xq, sx, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
+int wsvd_w8a8_prepare_factor(int E, int N, const void* A, wsvd_dtype A_dt, int8_t* AqT, float* sA,
+                             hipStream_t stream) {
+    if (E <= 0 || N <= 0) return WSVD_ERR_SHAPE;
+    if (!A || !AqT || !sA) return WSVD_ERR_NULL;
+    if (!act_dtype_ok(A_dt)) return WSVD_ERR_DTYPE;
+    if (!pow2_in(E, 256, 8192)) return WSVD_ERR_UNSUPPORTED;
+    if ((long long)E * N > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(AqT) || !aligned16(sA)) return WSVD_ERR_ALIGN;
+    return wsvd::launch_w8a8_prepare(E, N, A, A_dt, AqT, sA, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
+// Checks shared by both append entry points (everything but the operands).
+static int check_append_common(int nb, int E, int nh, int r, int L_cap, const int32_t* pos, void* C_K, void* C_V,
+                               wsvd_dtype C_dt, uint16_t* s_K, uint16_t* s_V, void* workspace,
+                               size_t workspace_bytes, int e_multiple) {
+    if (!pos || !C_K || !C_V) return WSVD_ERR_NULL;
     if (!cache_dtype_ok(C_dt)) return WSVD_ERR_DTYPE;
     if (C_dt == WSVD_I8) {
         if (!s_K || !s_V) return WSVD_ERR_NULL;
@@ -216,23 +239,24 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     } else if (s_K || s_V) {
         return WSVD_ERR_SHAPE;
     }
-    if (!rank_ok(r) || E % 256 != 0) return WSVD_ERR_UNSUPPORTED;
-    if ((long long)nb * nh * L_cap * r > (1ll << 46) || (long long)E * nh * r > (1ll << 40)) return WSVD_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(A_K) || !aligned16(A_V) || !aligned16(pos) || !aligned16(C_K) ||
-        !aligned16(C_V))
-        return WSVD_ERR_ALIGN;
+    if (!rank_ok(r) || E % e_multiple != 0) return WSVD_ERR_UNSUPPORTED;
+    if ((long long)nb * nh * L_cap * r > (1ll << 46) || (long long)E * nh * r > (1ll << 30) ||
+        (long long)nb * E > (1ll << 30))
+        return WSVD_ERR_SHAPE;
+    if (!aligned16(pos) || !aligned16(C_K) || !aligned16(C_V)) return WSVD_ERR_ALIGN;
     const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
     if (need > 0 && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return WSVD_ERR_WORKSPACE;
+    return WSVD_OK;
+}
 
-    wsvd::AppendArgs a;
+static wsvd::AppendArgs append_args(int nb, int E, int nh, int r, int L_cap, const int32_t* pos, void* C_K,
+                                    void* C_V, wsvd_dtype C_dt, uint16_t* s_K, uint16_t* s_V, void* workspace) {
+    wsvd::AppendArgs a{};
     a.nb = nb;
     a.E = E;
     a.nh = nh;
     a.r = r;
     a.L_cap = L_cap;
-    a.x = static_cast<const uint16_t*>(x);
-    a.A_K = static_cast<const uint16_t*>(A_K);
-    a.A_V = static_cast<const uint16_t*>(A_V);
     a.pos = pos;
     a.C_K = C_K;
     a.C_V = C_V;
@@ -240,9 +264,51 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     a.s_K = s_K;
     a.s_V = s_V;
     a.KS = wsvd::append_num_esplits(nb, E, nh, r);
+    const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
     const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
     a.part = need > 0 ? static_cast<float*>(workspace) : nullptr;
     a.counters = need > 0 ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + round_up(part, 256)) : nullptr;
+    return a;
+}
+
+int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap, const int8_t* xq, const float* sx,
+                            const int8_t* AqT_K, const int8_t* AqT_V, const float* sA_K, const float* sA_V,
+                            const int32_t* pos, void* C_K, void* C_V, wsvd_dtype C_dt, uint16_t* s_K,
+                            uint16_t* s_V, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0 || L_cap <= 0) return WSVD_ERR_SHAPE;
+    if (!xq || !sx || !AqT_K || !AqT_V || !sA_K || !sA_V) return WSVD_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(sx) || !aligned16(AqT_K) || !aligned16(AqT_V) || !aligned16(sA_K) ||
+        !aligned16(sA_V))
+        return WSVD_ERR_ALIGN;
+    const int st = check_append_common(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace,
+                                       workspace_bytes, 512);
+    if (st != WSVD_OK) return st;
+    wsvd::AppendArgs a = append_args(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace);
+    a.w8 = 1;
+    a.x = xq;
+    a.sx = sx;
+    a.A_K = AqT_K;
+    a.A_V = AqT_V;
+    a.sA_K = sA_K;
+    a.sA_V = sA_V;
+    return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
+int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, wsvd_dtype x_dt, const void* A_K,
+                       const void* A_V, wsvd_dtype A_dt, const int32_t* pos, void* C_K, void* C_V, wsvd_dtype C_dt,
+                       uint16_t* s_K, uint16_t* s_V, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0 || L_cap <= 0) return WSVD_ERR_SHAPE;
+    if (!x || !A_K || !A_V) return WSVD_ERR_NULL;
+    if (x_dt != WSVD_BF16 || A_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(A_K) || !aligned16(A_V)) return WSVD_ERR_ALIGN;
+    const int st = check_append_common(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace,
+                                       workspace_bytes, 256);
+    if (st != WSVD_OK) return st;
+    wsvd::AppendArgs a = append_args(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace);
+    a.w8 = 0;
+    a.x = x;
+    a.A_K = A_K;
+    a.A_V = A_V;
     return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 

@@ -37,6 +37,16 @@
 //    partials in slice order (so the result does not depend on which block
 //    finished last), resets the counter, rounds once to the cache dtype and
 //    writes row pos[b] of every head's K and V cache.
+//
+// W8A8 variant (w8): x arrives as int8 codes of the Hadamard-rotated token
+// with one fp32 scale per token, A as int8 codes of the rotated factor,
+// stored transposed ([nh r, E], k-contiguous) with one fp32 scale per
+// column (the pages' W8A8 setting with S1 outlier smoothing: German page
+// section 2C, Italian page section 2C, Arabic page section 2c).  Both
+// operands are k-contiguous, so both tiles are staged with whole-row loads
+// and no transpose, and v_mfma_i32_16x16x64_i8 accumulates exact int32
+// sums; the partial tiles are int32 (their sum is exact in any order).
+// The latent is acc * sx[b] * sA[n] in fp32, then stored as above.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
 
@@ -140,6 +150,53 @@ __device__ __forceinline__ void mma_stage(const Stage& s, uint16_t* sB, uint16_t
 }
 
 
+// ---- W8A8 operands: 512 k (bytes) per stage ---------------------------------
+constexpr int AP_ECB = 512;                 // int8 k per stage
+constexpr int AP_PITCHB = AP_ECB + 16;      // bytes per LDS row (same 528 as bf16)
+static_assert(AP_PITCHB == AP_PITCH * 2, "both variants share the LDS tiles");
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+struct TileCtxW8 {
+    __amdgpu_buffer_rsrc_t ra, rx;
+    uint32_t a_voff[8];  // bytes: row n_i of A^T (clamped to N1 - 1) * E + 16 * (tid & 31)
+    uint32_t x_voff[8];  // bytes: row m_i of x (clamped to nb - 1) * E + 16 * (tid & 31)
+};
+
+__device__ __forceinline__ void load_stage_w8(Stage& s, const TileCtxW8& c, int es) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.a_voff[i], es, kNonTemporal);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.x[i] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_voff[i], es, 0);
+}
+
+// Rows (tid >> 5) + 8 i of both tiles, 16 bytes at 16 (tid & 31); then
+// 8 k-steps of 64: lane l reads 16 bytes of row l % 16 at k 16 (l / 16) of
+// the step, for x (the wave's 16 rows) and for A (each 16-column group).
+__device__ __forceinline__ void mma_stage_w8(const Stage& s, uint8_t* sB, uint8_t* sX, i32x4 (&acc)[4], int tid,
+                                             int lane, int wave) {
+    __syncthreads();  // the previous stage's fragment reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = (tid >> 5) + 8 * i;
+        *reinterpret_cast<u32x4*>(&sB[row * AP_PITCHB + (tid & 31) * 16]) = s.a[i];
+        *reinterpret_cast<u32x4*>(&sX[row * AP_PITCHB + (tid & 31) * 16]) = s.x[i];
+    }
+    __syncthreads();
+    const uint8_t* xr = sX + (wave * 16 + (lane & 15)) * AP_PITCHB + (lane >> 4) * 16;
+    const uint8_t* br = sB + (lane & 15) * AP_PITCHB + (lane >> 4) * 16;
+#pragma unroll
+    for (int st = 0; st < AP_ECB / 64; ++st) {
+        const i32x4 xf = __builtin_bit_cast(i32x4, *reinterpret_cast<const u32x4*>(xr + st * 64));
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const i32x4 bf =
+                __builtin_bit_cast(i32x4, *reinterpret_cast<const u32x4*>(br + jn * 16 * AP_PITCHB + st * 64));
+            acc[jn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf, bf, acc[jn], 0, 0, 0);
+        }
+    }
+}
+
 // int8 cache rows (r in 16, 32, 64, so a head's r columns are whole
 // 16-column groups of one tile): per (row, head) the absmax over the head's
 // columns -- 16 lanes by DPP, then the head's column groups in registers --
@@ -183,6 +240,7 @@ __device__ __forceinline__ void store_int8_rows(const AppendArgs& a, const f32x4
     }
 }
 
+template <bool W8>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sB[AP_NT * AP_PITCH];
     __shared__ __attribute__((aligned(16))) uint16_t sX[AP_MT * AP_PITCH];
@@ -195,46 +253,78 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int ks = blockIdx.z;
     const int e_len = a.E / a.KS;
     const int e_beg = ks * e_len;
-    const int ns = e_len / AP_EC;
+    const int ns = e_len / (W8 ? AP_ECB : AP_EC);
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    TileCtx c;
-    c.ra = make_rsrc(kv ? a.A_V : a.A_K, (uint32_t)((size_t)a.E * N1 * 2));
-    c.rx = make_rsrc(a.x, (uint32_t)((size_t)a.nb * a.E * 2));
-    int ncol = n0 + (tid & 7) * 8;
-    if (ncol >= N1) ncol = 0;  // N1 is a multiple of 16, chunks are 8 wide
-    c.a_row = (uint32_t)N1 * 2u;
-    c.a_voff = ((uint32_t)(tid >> 3) * 8u * (uint32_t)N1 + (uint32_t)ncol) * 2u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        c.x_voff[i] = ((uint32_t)min(m0 + (tid >> 5) + 8 * i, a.nb - 1) * (uint32_t)a.E + (tid & 31) * 8u) * 2u;
-
+    // acc holds fp32 sums, or (W8) the bits of exact int32 sums until the
+    // scales are applied after the split-E reduction.
     f32x4 acc[4];
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Two stages (512 E rows) requested together; the split factor keeps a
-    // block's slice at one or two stages, so one pass normally covers it.
     Stage s0, s1;
-    for (int st = 0; st < ns; st += 2) {
-        load_stage(s0, c, e_beg + st * AP_EC);
-        if (st + 1 < ns) load_stage(s1, c, e_beg + (st + 1) * AP_EC);
-        mma_stage(s0, sB, sX, acc, tid, lane, wave);
-        if (st + 1 < ns) mma_stage(s1, sB, sX, acc, tid, lane, wave);
+    if constexpr (!W8) {
+        TileCtx c;
+        c.ra = make_rsrc(kv ? a.A_V : a.A_K, (uint32_t)((size_t)a.E * N1 * 2));
+        c.rx = make_rsrc(a.x, (uint32_t)((size_t)a.nb * a.E * 2));
+        int ncol = n0 + (tid & 7) * 8;
+        if (ncol >= N1) ncol = 0;  // N1 is a multiple of 16, chunks are 8 wide
+        c.a_row = (uint32_t)N1 * 2u;
+        c.a_voff = ((uint32_t)(tid >> 3) * 8u * (uint32_t)N1 + (uint32_t)ncol) * 2u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            c.x_voff[i] = ((uint32_t)min(m0 + (tid >> 5) + 8 * i, a.nb - 1) * (uint32_t)a.E + (tid & 31) * 8u) * 2u;
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Two stages (512 E rows) requested together; the split factor keeps
+        // a block's slice at one or two stages, so one pass normally covers it.
+        for (int st = 0; st < ns; st += 2) {
+            load_stage(s0, c, e_beg + st * AP_EC);
+            if (st + 1 < ns) load_stage(s1, c, e_beg + (st + 1) * AP_EC);
+            mma_stage(s0, sB, sX, acc, tid, lane, wave);
+            if (st + 1 < ns) mma_stage(s1, sB, sX, acc, tid, lane, wave);
+        }
+    } else {
+        TileCtxW8 c;
+        c.ra = make_rsrc(kv ? a.A_V : a.A_K, (uint32_t)((size_t)a.E * N1));
+        c.rx = make_rsrc(a.x, (uint32_t)((size_t)a.nb * a.E));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = (tid >> 5) + 8 * i;
+            c.a_voff[i] = (uint32_t)min(n0 + row, N1 - 1) * (uint32_t)a.E + (tid & 31) * 16u;
+            c.x_voff[i] = (uint32_t)min(m0 + row, a.nb - 1) * (uint32_t)a.E + (tid & 31) * 16u;
+        }
+        i32x4 iacc[4];
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) iacc[jn] = i32x4{0, 0, 0, 0};
+        uint8_t* bB = reinterpret_cast<uint8_t*>(sB);
+        uint8_t* bX = reinterpret_cast<uint8_t*>(sX);
+        for (int st = 0; st < ns; st += 2) {
+            load_stage_w8(s0, c, e_beg + st * AP_ECB);
+            if (st + 1 < ns) load_stage_w8(s1, c, e_beg + (st + 1) * AP_ECB);
+            mma_stage_w8(s0, bB, bX, iacc, tid, lane, wave);
+            if (st + 1 < ns) mma_stage_w8(s1, bB, bX, iacc, tid, lane, wave);
+        }
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[jn] = __builtin_bit_cast(f32x4, iacc[jn]);
     }
 
     // Rows of the caches this lane's accumulator entries go to (requested
     // only once the tile is complete, beside the last round of loads).
     int prow[4];
+    float xs[4], as[4];  // W8: this lane's row and column scales
     auto load_pos = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = m0 + wave * 16 + (lane >> 4) * 4 + i;
             prow[i] = (m < a.nb) ? a.pos[m] : -1;
+            if constexpr (W8) xs[i] = a.sx[min(m, a.nb - 1)];
+        }
+        if constexpr (W8) {
+            const float* sA = kv ? a.sA_V : a.sA_K;
+#pragma unroll
+            for (int jn = 0; jn < 4; ++jn) as[jn] = sA[min(n0 + jn * 16 + (lane & 15), N1 - 1)];
         }
     };
 
@@ -277,7 +367,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             for (int u = 0; u < 8; ++u) {
                 if (k0 + u < a.KS) {
 #pragma unroll
-                    for (int jn = 0; jn < 4; ++jn) sum[jn] += v[u][jn];
+                    for (int jn = 0; jn < 4; ++jn) {
+                        if constexpr (W8)
+                            sum[jn] = __builtin_bit_cast(f32x4, __builtin_bit_cast(i32x4, sum[jn]) +
+                                                                    __builtin_bit_cast(i32x4, v[u][jn]));
+                        else
+                            sum[jn] += v[u][jn];
+                    }
                 }
             }
         }
@@ -286,6 +382,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         for (int jn = 0; jn < 4; ++jn) acc[jn] = sum[jn];
     } else {
         load_pos();
+    }
+    if constexpr (W8) {  // exact integer sums -> latent values
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const i32x4 q = __builtin_bit_cast(i32x4, acc[jn]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[jn][i] = (float)q[i] * xs[i] * as[jn];
+        }
     }
 
     void* C = kv ? a.C_V : a.C_K;
@@ -314,8 +418,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 int append_num_esplits(int nb, int E, int nh, int r) {
     const long ntile = append_num_tiles(nb, nh, r);
     int ks = 1;
-    // >= 1.5 blocks per CU (256 CUs), E-slices a multiple of the LDS stage.
-    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2 * ks * AP_EC) == 0) ks *= 2;
+    // >= 1.5 blocks per CU (256 CUs); every E-slice a whole number of the
+    // larger (int8, 512 k) stage, so both variants split the same way and
+    // share one workspace size.
+    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2 * ks * AP_ECB) == 0) ks *= 2;
     return ks;
 }
 
@@ -332,7 +438,10 @@ size_t append_partial_bytes(int nb, int E, int nh, int r) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     const int N1 = a.nh * a.r;
     dim3 g((N1 + AP_NT - 1) / AP_NT, 2 * ((a.nb + AP_MT - 1) / AP_MT), a.KS);
-    hipLaunchKernelGGL(append_kernel, g, dim3(256), 0, st, a);
+    if (a.w8)
+        hipLaunchKernelGGL(append_kernel<true>, g, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(append_kernel<false>, g, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,127 @@
+// w8a8.hip -- the integer operands of the W8A8 append.
+//
+// The pages run the projections at W8A8 and smooth activation outliers with
+// an orthogonal Hadamard rotation S1 before quantising ("WSVD: Weighted
+// Low-Rank Approximation for Fast and Efficient Execution of Low-Precision
+// Vision-Language Models": German page section 2C, Italian page section 2C,
+// Japanese page section 2.3, Arabic page section 2c).  S1 here is the
+// normalised Walsh-Hadamard matrix H = H_E / sqrt(E) (Sylvester order, E a
+// power of two); it is symmetric and orthogonal, so x . A = (x H) . (H A)
+// and the rotation of A is folded offline.
+//
+//  * quantize_rows: per token, x~ = x H by an in-place fast Walsh-Hadamard
+//    transform in LDS (log2 E butterfly passes, fp32), then symmetric absmax
+//    codes with one fp32 scale: s = max|x~| / 127, code =
+//    clamp(round_half_even(x~ / s), -127, 127), all zero if s == 0.
+//  * prepare: offline, per output column n of a factor A [E, N]: the same
+//    transform down the column, the same codes with one fp32 scale per
+//    column, written transposed (A^T codes [N, E], k-contiguous) so the
+//    append's integer MFMA reads both operands without a transpose.
+//
+// Both are small, one-off passes (the activations are nb x E values); one
+// workgroup owns whole rows so the transform needs no cross-block traffic.
+#include "wsvd_common.hpp"
+#include "wsvd_internal.hpp"
+
+namespace wsvd {
+
+// In-place unnormalised Walsh-Hadamard transform of `cols` length-E vectors
+// stored back to back in LDS (E a power of two): pass h pairs element i
+// with i + h inside each block of 2h and writes (a + b, a - b).
+__device__ __forceinline__ void fwht_lds(float* L, int E, int cols) {
+    const int half = E >> 1;
+    for (int h = 1; h < E; h <<= 1) {
+        __syncthreads();
+        for (int p = threadIdx.x; p < cols * half; p += blockDim.x) {
+            const int c = p / half;
+            const int q = p - c * half;
+            const int i = ((q & ~(h - 1)) << 1) | (q & (h - 1));
+            float* v = L + (size_t)c * E;
+            const float x0 = v[i], x1 = v[i + h];
+            v[i] = x0 + x1;
+            v[i + h] = x0 - x1;
+        }
+    }
+    __syncthreads();
+}
+
+// Maximum over the workgroup (256 threads); every thread gets it.
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ int8_t code_of(float v, float s) {
+    if (!(s > 0.f)) return 0;
+    return (int8_t)(int)fminf(fmaxf(__builtin_rintf(v / s), -127.f), 127.f);
+}
+
+__global__ __launch_bounds__(256) void w8a8_quantize_rows_kernel(const void* x, int x_dt, int E, float inv_sqrt_e,
+                                                                 int8_t* xq, float* sx) {
+    extern __shared__ float L[];
+    __shared__ float red[4];
+    const size_t b = blockIdx.x;
+    for (int i = threadIdx.x; i < E; i += 256) L[i] = load_elem(x, x_dt, b * E + i);
+    fwht_lds(L, E, 1);
+    float m = 0.f;
+    for (int i = threadIdx.x; i < E; i += 256) {
+        const float v = L[i] * inv_sqrt_e;
+        L[i] = v;
+        m = fmaxf(m, fabsf(v));
+    }
+    const float s = block_max(m, red) / 127.f;
+    for (int i = threadIdx.x; i < E; i += 256) xq[b * E + i] = code_of(L[i], s);
+    if (threadIdx.x == 0) sx[b] = s;
+}
+
+__global__ __launch_bounds__(256) void w8a8_prepare_kernel(const void* A, int A_dt, int E, int N, int cols,
+                                                           float inv_sqrt_e, int8_t* AqT, float* sA) {
+    extern __shared__ float L[];  // [cols][E]
+    __shared__ float red[4];
+    const int n0 = blockIdx.x * cols;
+    for (int idx = threadIdx.x; idx < cols * E; idx += 256) {
+        const int e = idx / cols;
+        const int c = idx - e * cols;
+        L[(size_t)c * E + e] = (n0 + c < N) ? load_elem(A, A_dt, (size_t)e * N + n0 + c) : 0.f;
+    }
+    fwht_lds(L, E, cols);
+    for (int c = 0; c < cols && n0 + c < N; ++c) {
+        float* v = L + (size_t)c * E;
+        float m = 0.f;
+        for (int e = threadIdx.x; e < E; e += 256) {
+            const float t = v[e] * inv_sqrt_e;
+            v[e] = t;
+            m = fmaxf(m, fabsf(t));
+        }
+        const float s = block_max(m, red) / 127.f;
+        int8_t* out = AqT + (size_t)(n0 + c) * E;
+        for (int e = threadIdx.x; e < E; e += 256) out[e] = code_of(v[e], s);
+        if (threadIdx.x == 0) sA[n0 + c] = s;
+    }
+}
+
+// At most 32 KB of LDS per workgroup: cols * E floats.
+int w8a8_prepare_cols(int E) { return E >= 8192 ? 1 : min(8, 8192 / E); }
+
+hipError_t launch_w8a8_quantize_rows(int nb, int E, const void* x, int x_dt, int8_t* xq, float* sx,
+                                     hipStream_t st) {
+    const float inv = (float)(1.0 / __builtin_sqrt((double)E));
+    hipLaunchKernelGGL(w8a8_quantize_rows_kernel, dim3(nb), dim3(256), (size_t)E * sizeof(float), st, x, x_dt, E,
+                       inv, xq, sx);
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a8_prepare(int E, int N, const void* A, int A_dt, int8_t* AqT, float* sA, hipStream_t st) {
+    const int cols = w8a8_prepare_cols(E);
+    const float inv = (float)(1.0 / __builtin_sqrt((double)E));
+    const size_t lds = (size_t)cols * E * sizeof(float);
+    hipLaunchKernelGGL(w8a8_prepare_kernel, dim3((N + cols - 1) / cols), dim3(256), lds, st, A, A_dt, E, N, cols,
+                       inv, AqT, sA);
+    return hipGetLastError();
+}
+
+}  // namespace wsvd

@@ -39,9 +39,14 @@ hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, con
 
 struct AppendArgs {
     int nb, E, nh, r, L_cap;
-    const uint16_t* x;    // bf16 [nb, E]
-    const uint16_t* A_K;  // bf16 [E, nh*r]
-    const uint16_t* A_V;
+    int w8;               // 0: bf16 x [nb, E], A [E, nh*r]
+                          // 1: int8 x codes [nb, E] + sx, int8 A^T codes [nh*r, E] + sA
+    const void* x;
+    const void* A_K;
+    const void* A_V;
+    const float* sx;      // fp32 [nb]      (w8 only)
+    const float* sA_K;    // fp32 [nh*r]    (w8 only)
+    const float* sA_V;
     const int32_t* pos;
     void* C_K;
     void* C_V;
@@ -54,6 +59,14 @@ struct AppendArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+// W8A8 helpers (w8a8.hip): S1 rotation + per-row int8 codes of activations,
+// and the offline rotation + per-column int8 codes of a factor.
+hipError_t launch_w8a8_quantize_rows(int nb, int E, const void* x, int x_dt, int8_t* xq, float* sx,
+                                     hipStream_t st);
+hipError_t launch_w8a8_prepare(int E, int N, const void* A, int A_dt, int8_t* AqT, float* sA, hipStream_t st);
+// Columns of A one prepare block rotates at once (LDS holds cols * E floats).
+int w8a8_prepare_cols(int E);
 
 // Split-E factor the append kernel uses for these sizes (host).
 int append_num_esplits(int nb, int E, int nh, int r);

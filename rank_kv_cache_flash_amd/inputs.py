@@ -198,3 +198,31 @@ def make_ragged_step_inputs(nb, nh, H, r, E, L_lo, L_hi, L_cap, *, seed, q_gain=
     inp.A_K, inp.A_V, inp.A_dt = _store(A_K, dt), _store(A_V, dt), dt
     inp.pos = (L - 1).astype(np.int32)
     return inp
+
+
+# ---------------------------------------------------------------------------
+# W8A8 projection inputs
+# ---------------------------------------------------------------------------
+T_XO, T_XQ, T_SX, T_AQ, T_SA = range(20, 25)
+
+
+def make_w8a8_activations(nb, E, *, seed, outlier_channels=0.01, outlier_mul=20.0, dt="bf16"):
+    """Token activations x [nb, E] ~ N(0, 1)/sqrt(E) with a few outlier
+    channels (the same seeded 1 % of the E columns scaled by outlier_mul in
+    every token), the structure the pages' rotation is meant to smooth."""
+    x = _normal(seed, (T_X,), (nb, E), 1.0 / np.sqrt(E))
+    cols = _rng(seed, T_XO).random(E) < outlier_channels
+    x[:, cols] *= np.float32(outlier_mul)
+    return _store(x, dt)
+
+
+def make_w8a8_codes(nb, E, N, *, seed):
+    """Synthetic integer operands of the W8A8 product: token codes xq [nb, E],
+    per-token scales sx [nb], transposed factor codes AqT [N, E] and
+    per-column scales sA [N].  Codes are uniform in [-127, 127]; scales are
+    positive and spread over a few octaves."""
+    xq = _rng(seed, T_XQ).integers(-127, 128, size=(nb, E), dtype=np.int8)
+    AqT = _rng(seed, T_AQ).integers(-127, 128, size=(N, E), dtype=np.int8)
+    sx = (np.exp2(_rng(seed, T_SX).uniform(-12, -8, size=nb))).astype(np.float32)
+    sA = (np.exp2(_rng(seed, T_SA).uniform(-10, -6, size=N))).astype(np.float32)
+    return xq, sx, AqT, sA

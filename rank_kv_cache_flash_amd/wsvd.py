@@ -46,6 +46,13 @@ def lib() -> ctypes.CDLL:
     L.wsvd_append_latent.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, vp,
                                      vp, sz, vp]
     L.wsvd_append_latent.restype = i32
+    L.wsvd_append_latent_w8a8.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                          vp, sz, vp]
+    L.wsvd_append_latent_w8a8.restype = i32
+    L.wsvd_w8a8_quantize_activations.argtypes = [i32, i32, vp, i32, vp, vp, vp]
+    L.wsvd_w8a8_quantize_activations.restype = i32
+    L.wsvd_w8a8_prepare_factor.argtypes = [i32, i32, vp, i32, vp, vp, vp]
+    L.wsvd_w8a8_prepare_factor.restype = i32
     L.wsvd_decode_num_splits.argtypes = [i32, i32, i32, i32]
     L.wsvd_decode_num_splits.restype = i32
     L.wsvd_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -231,6 +238,49 @@ def append_latent(x, A_K, A_V, pos, C_K, C_V, *, s_K=None, s_V=None, workspace=N
                                   _ptr(pos), _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], _ptr(s_K), _ptr(s_V),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "wsvd_append_latent")
+    return C_K, C_V
+
+
+def w8a8_prepare_factor(A, *, stream=None):
+    """wsvd_w8a8_prepare_factor: A [E, N] -> (AqT int8 [N, E], sA float32 [N])."""
+    _dev(A, "A")
+    E, N = A.shape
+    AqT = torch.empty((N, E), dtype=torch.int8, device=A.device)
+    sA = torch.empty((N,), dtype=torch.float32, device=A.device)
+    _check(lib().wsvd_w8a8_prepare_factor(E, N, _ptr(A), _DT[A.dtype], _ptr(AqT), _ptr(sA), _stream(stream)),
+           "wsvd_w8a8_prepare_factor")
+    return AqT, sA
+
+
+def w8a8_quantize_activations(x, *, xq=None, sx=None, stream=None):
+    """wsvd_w8a8_quantize_activations: x [nb, E] -> (xq int8 [nb, E], sx float32 [nb])."""
+    _dev(x, "x")
+    nb, E = x.shape
+    xq = torch.empty((nb, E), dtype=torch.int8, device=x.device) if xq is None else xq
+    sx = torch.empty((nb,), dtype=torch.float32, device=x.device) if sx is None else sx
+    _dev(xq, "xq")
+    _dev(sx, "sx")
+    _check(lib().wsvd_w8a8_quantize_activations(nb, E, _ptr(x), _DT[x.dtype], _ptr(xq), _ptr(sx), _stream(stream)),
+           "wsvd_w8a8_quantize_activations")
+    return xq, sx
+
+
+def append_latent_w8a8(xq, sx, AqT_K, sA_K, AqT_V, sA_V, pos, C_K, C_V, *, s_K=None, s_V=None, workspace=None,
+                       stream=None):
+    """wsvd_append_latent_w8a8: int8 token codes + scales and int8 transposed factor codes + scales;
+    caches [nb, nh, L_cap, r] written in place at row pos[b]."""
+    for t, n in ((xq, "xq"), (sx, "sx"), (AqT_K, "AqT_K"), (sA_K, "sA_K"), (AqT_V, "AqT_V"), (sA_V, "sA_V"),
+                 (pos, "pos"), (C_K, "C_K"), (C_V, "C_V"), (s_K, "s_K"), (s_V, "s_V"), (workspace, "workspace")):
+        _dev(t, n)
+    nb, E = xq.shape
+    _, nh, L_cap, r = C_K.shape
+    if workspace is None:
+        workspace = append_workspace(nb, E, nh, r, device=xq.device)
+    st = lib().wsvd_append_latent_w8a8(nb, E, nh, r, L_cap, _ptr(xq), _ptr(sx), _ptr(AqT_K), _ptr(AqT_V),
+                                       _ptr(sA_K), _ptr(sA_V), _ptr(pos), _ptr(C_K), _ptr(C_V), _DT[C_K.dtype],
+                                       _ptr(s_K), _ptr(s_V), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "wsvd_append_latent_w8a8")
     return C_K, C_V
 
 

@@ -169,3 +169,42 @@ def dense(L, **kw):
 ])
 def test_dense_rejects(L, kw, want):
     assert dense(L, **kw) == want
+
+
+def test_w8a8_rejects(L):
+    v = ctypes.c_void_p
+    q = L.wsvd_w8a8_quantize_activations
+    assert q(0, 4096, v(P), BF16, v(P), v(P), None) == ESHAPE
+    assert q(2, 4096, None, BF16, v(P), v(P), None) == ENULL
+    assert q(2, 4096, v(P), I8, v(P), v(P), None) == EDTYPE
+    assert q(2, 3000, v(P), BF16, v(P), v(P), None) == EUNSUP       # not a power of two
+    assert q(2, 16384, v(P), BF16, v(P), v(P), None) == EUNSUP      # above the LDS limit
+    assert q(2, 128, v(P), BF16, v(P), v(P), None) == EUNSUP
+    assert q(2, 4096, v(P + 2), BF16, v(P), v(P), None) == EALIGN
+    p = L.wsvd_w8a8_prepare_factor
+    assert p(4096, 0, v(P), BF16, v(P), v(P), None) == ESHAPE
+    assert p(4096, 64, v(P), BF16, None, v(P), None) == ENULL
+    assert p(4096, 64, v(P), I8, v(P), v(P), None) == EDTYPE
+    assert p(1000, 64, v(P), BF16, v(P), v(P), None) == EUNSUP
+    assert p(4096, 64, v(P), BF16, v(P), v(P + 4), None) == EALIGN
+
+
+def append_w8(L, **kw):
+    a = dict(nb=64, E=4096, nh=32, r=32, L_cap=8192, xq=P, sx=P, AK=P, AV=P, sK=P, sV=P, pos=P, C_K=P, C_V=P,
+             C_dt=BF16, s_K=None, s_V=None, ws=P, ws_bytes=WS)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return L.wsvd_append_latent_w8a8(a["nb"], a["E"], a["nh"], a["r"], a["L_cap"], v(a["xq"]), v(a["sx"]),
+                                     v(a["AK"]), v(a["AV"]), v(a["sK"]), v(a["sV"]), v(a["pos"]), v(a["C_K"]),
+                                     v(a["C_V"]), a["C_dt"], v(a["s_K"]), v(a["s_V"]), v(a["ws"]), a["ws_bytes"],
+                                     None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), ESHAPE), (dict(xq=None), ENULL), (dict(sV=None), ENULL), (dict(pos=None), ENULL),
+    (dict(C_dt=F16), EDTYPE), (dict(C_dt=I8), ENULL), (dict(C_dt=I8, s_K=P, s_V=P, r=48), EUNSUP),
+    (dict(E=4096 + 256), EUNSUP), (dict(r=24), EUNSUP), (dict(AK=P + 8), EALIGN), (dict(sx=P + 4), EALIGN),
+    ({}, EWS), (dict(ws=None), EWS), (dict(C_dt=I8, s_K=P, s_V=P), EWS),
+])
+def test_append_w8a8_rejects(L, kw, want):
+    assert append_w8(L, **kw) == want
