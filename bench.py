@@ -162,6 +162,57 @@ def load_traffic(workload_name, launches_bytes):
 
 
 # ---------------------------------------------------------------------------
+# append alone: bf16 operands vs the W8A8 path (rotate + quantise x, int8 product)
+# ---------------------------------------------------------------------------
+def append_variants(cfg, steps, warmup=10, seed=0):
+    """Time the append of one step alone at cfg's shapes (bf16 caches), with
+    bf16 x and A and with the W8A8 path (wsvd_w8a8_quantize_activations +
+    wsvd_append_latent_w8a8 on offline-prepared int8 factors).  Random GPU
+    inputs (timing only; parity is in the tests), rotating over copies of the
+    factors so A is read from HBM, graph replay."""
+    import torch
+    from rank_kv_cache_flash_amd import wsvd
+
+    nb, E, nh, r, L_cap = cfg.nb, cfg.E, cfg.nh, cfg.r, cfg.L_cap
+    N = nh * r
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    bf = torch.bfloat16
+    x = (torch.randn(nb, E, generator=g, device="cuda") * E ** -0.5).to(bf)
+    pos = torch.randint(0, L_cap, (nb,), generator=g, device="cuda", dtype=torch.int32)
+    C_K = torch.zeros(nb, nh, L_cap, r, dtype=bf, device="cuda")
+    C_V = torch.zeros_like(C_K)
+    ws = wsvd.append_workspace(nb, E, nh, r)
+    ncopy = 8
+    bf_calls, w8_facs = [], []
+    for _ in range(ncopy):
+        AK = (torch.randn(E, N, generator=g, device="cuda") * r ** -0.5).to(bf)
+        AV = (torch.randn(E, N, generator=g, device="cuda") * r ** -0.5).to(bf)
+        bf_calls.append(wsvd.PreparedAppend(x, AK, AV, pos, C_K, C_V, workspace=ws))
+        w8_facs.append((*wsvd.w8a8_prepare_factor(AK), *wsvd.w8a8_prepare_factor(AV)))
+    xq = torch.empty(nb, E, dtype=torch.int8, device="cuda")
+    sx = torch.empty(nb, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    t_bf = graph_time(lambda i: bf_calls[i % ncopy](torch.cuda.current_stream()), steps, warmup)[0]
+
+    def w8_step(i):
+        AKq, sAK, AVq, sAV = w8_facs[i % ncopy]
+        wsvd.w8a8_quantize_activations(x, xq=xq, sx=sx)
+        wsvd.append_latent_w8a8(xq, sx, AKq, sAK, AVq, sAV, pos, C_K, C_V, workspace=ws)
+
+    t_w8 = graph_time(w8_step, steps, warmup)[0]
+    t_q = graph_time(lambda i: wsvd.w8a8_quantize_activations(x, xq=xq, sx=sx), steps, warmup)[0]
+    b_bf = 2 * E * N * 2 + nb * E * 2 + nb * 2 * N * 2
+    b_w8 = 2 * E * N + 2 * N * 4 + nb * E * (2 + 1) + nb * 4 + nb * 2 * N * 2
+    del bf_calls, w8_facs
+    torch.cuda.empty_cache()
+    return {"shape": f"x[{nb},{E}] -> {nh} heads x r {r}, bf16 caches",
+            "bf16_us": round(t_bf * 1e6, 3), "w8a8_us": round(t_w8 * 1e6, 3),
+            "w8a8_quantize_x_us": round(t_q * 1e6, 3),
+            "bf16_bytes": b_bf, "w8a8_bytes": b_w8,
+            "bf16_GB_per_s": round(b_bf / t_bf / 1e9, 1), "w8a8_GB_per_s": round(b_w8 / t_w8 / 1e9, 1)}
+
+
+# ---------------------------------------------------------------------------
 # dense Flash-Decoding baseline at the same shape (the pages' comparison)
 # ---------------------------------------------------------------------------
 def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
@@ -433,6 +484,8 @@ def main():
         per[c.name]["steps"] = k
         del wc
         torch.cuda.empty_cache()
+        if c.has_append:
+            per[c.name]["append_alone"] = append_variants(c, max(k, 100), min(args.warmup, 10))
 
     line = {
         "metric": METRIC,

@@ -9,10 +9,11 @@
 // power of two); it is symmetric and orthogonal, so x . A = (x H) . (H A)
 // and the rotation of A is folded offline.
 //
-//  * quantize_rows: per token, x~ = x H by an in-place fast Walsh-Hadamard
-//    transform in LDS (log2 E butterfly passes, fp32), then symmetric absmax
-//    codes with one fp32 scale: s = max|x~| / 127, code =
-//    clamp(round_half_even(x~ / s), -127, 127), all zero if s == 0.
+//  * quantize_rows: per token, x~ = x H by a fast Walsh-Hadamard transform
+//    (log2 E butterfly passes, fp32: in registers, across lanes, then once
+//    through LDS), then symmetric absmax codes with one fp32 scale:
+//    s = max|x~| / 127, code = clamp(round_half_even(x~ / s), -127, 127),
+//    all zero if s == 0.
 //  * prepare: offline, per output column n of a factor A [E, N]: the same
 //    transform down the column, the same codes with one fp32 scale per
 //    column, written transposed (A^T codes [N, E], k-contiguous) so the
@@ -26,6 +27,7 @@
 namespace wsvd {
 
 // In-place unnormalised Walsh-Hadamard transform of `cols` length-E vectors
+// (the offline factor pass)
 // stored back to back in LDS (E a power of two): pass h pairs element i
 // with i + h inside each block of 2h and writes (a + b, a - b).
 __device__ __forceinline__ void fwht_lds(float* L, int E, int cols) {
@@ -60,22 +62,83 @@ __device__ __forceinline__ int8_t code_of(float v, float s) {
     return (int8_t)(int)fminf(fmaxf(__builtin_rintf(v / s), -127.f), 127.f);
 }
 
-__global__ __launch_bounds__(256) void w8a8_quantize_rows_kernel(const void* x, int x_dt, int E, float inv_sqrt_e,
-                                                                 int8_t* xq, float* sx) {
-    extern __shared__ float L[];
+// One token per workgroup.  Thread t holds EPT = E / 256 consecutive
+// elements, so the transform's passes split by distance: inside a thread's
+// registers (distance < EPT), across the lanes of a wave (shuffles), and the
+// last two passes (distances E/4 and E/2, between the 4 waves) as one 4-point
+// transform per column after a single trip through LDS.
+// Element i of a tensor of compile-time dtype DT, as float (straight-line
+// loads: a runtime dtype switch per element serialised them).
+template <int DT>
+__device__ __forceinline__ float elem(const void* p, size_t i) {
+    if constexpr (DT == WSVD_F32) return static_cast<const float*>(p)[i];
+    else if constexpr (DT == WSVD_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    else return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+template <int EPT, int DT>
+__global__ __launch_bounds__(256) void w8a8_quantize_rows_kernel(const void* x, float inv_sqrt_e, int8_t* xq,
+                                                                 float* sx) {
+    constexpr int E = EPT * 256;
+    constexpr int Q = E / 4;  // one wave's span
+    __shared__ float L[E];
     __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const size_t b = blockIdx.x;
-    for (int i = threadIdx.x; i < E; i += 256) L[i] = load_elem(x, x_dt, b * E + i);
-    fwht_lds(L, E, 1);
+    float v[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) v[k] = elem<DT>(x, b * E + (size_t)tid * EPT + k);
+    // passes inside the thread
+#pragma unroll
+    for (int h = 1; h < EPT; h <<= 1) {
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            if (k & h) continue;
+            const float a0 = v[k], a1 = v[k + h];
+            v[k] = a0 + a1;
+            v[k + h] = a0 - a1;
+        }
+    }
+    // passes across lanes: element distance EPT * d
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const bool upper = (lane & d) != 0;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const float y = __shfl_xor(v[k], d, 64);
+            v[k] = upper ? (y - v[k]) : (v[k] + y);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) L[tid * EPT + k] = v[k];
+    __syncthreads();
+    // last two passes: column j of the four wave spans, j = tid + 256 i
+    constexpr int NJ = (Q + 255) / 256;
+    float o[NJ][4];
     float m = 0.f;
-    for (int i = threadIdx.x; i < E; i += 256) {
-        const float v = L[i] * inv_sqrt_e;
-        L[i] = v;
-        m = fmaxf(m, fabsf(v));
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) {
+        const int j = tid + 256 * i;
+        if (j >= Q) break;
+        const float a0 = L[j], a1 = L[j + Q], a2 = L[j + 2 * Q], a3 = L[j + 3 * Q];
+        const float s01 = a0 + a1, d01 = a0 - a1, s23 = a2 + a3, d23 = a2 - a3;
+        o[i][0] = (s01 + s23) * inv_sqrt_e;
+        o[i][1] = (d01 + d23) * inv_sqrt_e;
+        o[i][2] = (s01 - s23) * inv_sqrt_e;
+        o[i][3] = (d01 - d23) * inv_sqrt_e;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m = fmaxf(m, fabsf(o[i][c]));
     }
     const float s = block_max(m, red) / 127.f;
-    for (int i = threadIdx.x; i < E; i += 256) xq[b * E + i] = code_of(L[i], s);
-    if (threadIdx.x == 0) sx[b] = s;
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) {
+        const int j = tid + 256 * i;
+        if (j >= Q) break;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xq[b * E + j + c * Q] = code_of(o[i][c], s);
+    }
+    if (tid == 0) sx[b] = s;
 }
 
 __global__ __launch_bounds__(256) void w8a8_prepare_kernel(const void* A, int A_dt, int E, int N, int cols,
@@ -107,11 +170,28 @@ __global__ __launch_bounds__(256) void w8a8_prepare_kernel(const void* A, int A_
 // At most 32 KB of LDS per workgroup: cols * E floats.
 int w8a8_prepare_cols(int E) { return E >= 8192 ? 1 : min(8, 8192 / E); }
 
+template <int EPT>
+static void launch_qr(int nb, const void* x, int x_dt, float inv, int8_t* xq, float* sx, hipStream_t st) {
+    if (x_dt == WSVD_F32)
+        hipLaunchKernelGGL((w8a8_quantize_rows_kernel<EPT, WSVD_F32>), dim3(nb), dim3(256), 0, st, x, inv, xq, sx);
+    else if (x_dt == WSVD_BF16)
+        hipLaunchKernelGGL((w8a8_quantize_rows_kernel<EPT, WSVD_BF16>), dim3(nb), dim3(256), 0, st, x, inv, xq, sx);
+    else
+        hipLaunchKernelGGL((w8a8_quantize_rows_kernel<EPT, WSVD_F16>), dim3(nb), dim3(256), 0, st, x, inv, xq, sx);
+}
+
 hipError_t launch_w8a8_quantize_rows(int nb, int E, const void* x, int x_dt, int8_t* xq, float* sx,
                                      hipStream_t st) {
     const float inv = (float)(1.0 / __builtin_sqrt((double)E));
-    hipLaunchKernelGGL(w8a8_quantize_rows_kernel, dim3(nb), dim3(256), (size_t)E * sizeof(float), st, x, x_dt, E,
-                       inv, xq, sx);
+    switch (E) {
+        case 256: launch_qr<1>(nb, x, x_dt, inv, xq, sx, st); break;
+        case 512: launch_qr<2>(nb, x, x_dt, inv, xq, sx, st); break;
+        case 1024: launch_qr<4>(nb, x, x_dt, inv, xq, sx, st); break;
+        case 2048: launch_qr<8>(nb, x, x_dt, inv, xq, sx, st); break;
+        case 4096: launch_qr<16>(nb, x, x_dt, inv, xq, sx, st); break;
+        case 8192: launch_qr<32>(nb, x, x_dt, inv, xq, sx, st); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
