@@ -201,6 +201,46 @@ def _qrows_f32_floor(v):
     return np.clip(q, -127, 127).astype(np.int8), scale
 
 
+def _rope_adjacent_pairs(X, positions, base=10000.0):
+    X = np.asarray(X, dtype=np.float64)
+    H = X.shape[-1]
+    a = oracle.rope.rope_angles(positions, H, base)
+    c, s_ = np.cos(a), np.sin(a)
+    x1, x2 = X[..., 0::2], X[..., 1::2]
+    out = np.empty_like(X)
+    out[..., 0::2], out[..., 1::2] = x1 * c - x2 * s_, x2 * c + x1 * s_
+    return out
+
+
+def _rope_sin_flipped(X, positions, base=10000.0):
+    X = np.asarray(X, dtype=np.float64)
+    H = X.shape[-1]
+    a = oracle.rope.rope_angles(positions, H, base)
+    c, s_ = np.cos(a), np.sin(a)
+    x1, x2 = X[..., : H // 2], X[..., H // 2:]
+    return np.concatenate([x1 * c + x2 * s_, x2 * c - x1 * s_], axis=-1)
+
+
+def _rope_theta_half(positions, H, base=10000.0):
+    i = np.arange(H // 2, dtype=np.float64)
+    return np.asarray(positions, dtype=np.float64)[:, None] * (base ** (-i / H))[None, :]
+
+
+def _decode_rope_from_one(inp, base=10000.0, softmax_scale=None, pairs=None, _orig=None):
+    import copy
+    from oracle import rope as Rm
+    nb, nh, H = inp.q.shape
+    out = np.zeros((nb, nh, H))
+    for b in range(nb):
+        for h in range(nh):
+            ell = int(inp.L[b])
+            K = W.reconstruct(W.dequant_latent(inp.C_K[b, h, :ell], inp.C_dt), W.upcast(inp.B_K[h], inp.B_dt))
+            V = W.reconstruct(W.dequant_latent(inp.C_V[b, h, :ell], inp.C_dt), W.upcast(inp.B_V[h], inp.B_dt))
+            K = Rm.rope_rotate(K, np.arange(1, ell + 1), base)
+            out[b, h] = W.attend(W.upcast(inp.q[b, h], inp.q_dt), K, V, 1 / np.sqrt(H))
+    return out
+
+
 MUTANTS = {
     "softmax without max shift": ("softmax_weights", _softmax_nomax),
     "softmax sign flipped": ("softmax_weights", _softmax_sign),
@@ -227,6 +267,10 @@ MUTANTS = {
     "rotation not normalised": ("rotate_rows", _rotate_unnormalised),
     "w8a8 weight scale dropped": ("w8a8_latents", _w8a8_drop_weight_scale),
     "fp32-scale codes truncated": ("quantize_rows_f32", _qrows_f32_floor),
+    "rope pairs adjacent elements": ("rope_rotate", _rope_adjacent_pairs),
+    "rope sine sign flipped": ("rope_rotate", _rope_sin_flipped),
+    "rope frequency exponent halved": ("rope_angles", _rope_theta_half),
+    "rope positions start at 1": ("decode_attn_rope", _decode_rope_from_one),
 }
 
 
@@ -234,7 +278,8 @@ MUTANTS = {
 def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     import oracle.w8a8 as W8
-    for mod in (W, W8, oracle):
+    import oracle.rope as WR
+    for mod in (W, W8, WR, oracle):
         if hasattr(mod, attr):
             monkeypatch.setattr(mod, attr, fn)
     caught = []

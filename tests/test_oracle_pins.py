@@ -483,3 +483,62 @@ def test_w8a8_exact_case_and_error_bound():
     Ar = (scipy.linalg.hadamard(E) @ A) / np.sqrt(E)
     bound = (sx[:, None] / 2) @ np.abs(Ar).sum(0)[None, :] + np.abs(xr).sum(1)[:, None] * (sA[None, :] / 2) * (1 + 1e-6)
     assert np.all(np.abs(c - x @ A) <= bound * 1.01 + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# rotary position step on reconstructed keys
+# ---------------------------------------------------------------------------
+def test_rope_hand_worked():
+    # H = 4, base 16: theta = (1, 16^-1/2 = 1/4).  At t = 2 pi pair (0, 2) turns a full circle
+    # and pair (1, 3) a quarter: (x1, x3) -> (-x3, x1).
+    got = O.rope_rotate(np.array([[1.0, 2.0, 3.0, 4.0]]), [2 * math.pi], base=16.0)
+    assert np.allclose(got, [[1.0, -4.0, 3.0, 2.0]], atol=1e-12)
+    # t = 0 is the identity
+    x = RNG.standard_normal((3, 8))
+    assert np.array_equal(O.rope_rotate(x, [0, 0, 0]), x)
+
+
+def test_rope_rotation_properties():
+    H = 64
+    q = RNG.standard_normal(H)
+    k = RNG.standard_normal(H)
+    X = RNG.standard_normal((5, H))
+    t = np.array([0, 3, 17, 250, 4095])
+    R = O.rope_rotate(X, t)
+    assert np.allclose(np.linalg.norm(R, axis=1), np.linalg.norm(X, axis=1), rtol=1e-12)
+    assert np.allclose(O.rope_rotate(R, t + 5), O.rope_rotate(X, 2 * t + 5), atol=1e-9)
+    for m, n in [(10, 3), (1000, 999), (7, 7)]:
+        lhs = O.rope_rotate(q[None], [m]) @ O.rope_rotate(k[None], [n]).T
+        rhs = O.rope_rotate(q[None], [m - n]) @ k[None].T
+        assert np.allclose(lhs, rhs, rtol=1e-9, atol=1e-9)
+
+
+def test_rope_matches_explicit_plane_rotations():
+    # each pair (i, i + H/2) is an explicit 2x2 rotation by t * base^(-2 i / H)
+    H, base = 8, 100.0
+    x = RNG.standard_normal(H)
+    for t in (1, 6, 33):
+        want = np.empty(H)
+        for i in range(H // 2):
+            a = t * base ** (-2.0 * i / H)
+            rot = np.array([[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]])
+            want[i], want[i + H // 2] = rot @ np.array([x[i], x[i + H // 2]])
+        assert np.allclose(O.rope_rotate(x[None], [t], base=base)[0], want, atol=1e-12)
+
+
+def test_rope_decode_one_token_and_brute_force():
+    rng = np.random.default_rng(31)
+    nh, H, r, L = 2, 8, 4, 5
+    q = rng.standard_normal((nh, H))
+    CK, CV = rng.standard_normal((nh, L, r)), rng.standard_normal((nh, L, r))
+    BK, BV = rng.standard_normal((nh, r, H)), rng.standard_normal((nh, r, H))
+    inp = _inp_f64(q, CK, CV, BK, BV)
+    got = O.decode_attn_rope(inp, base=50.0)
+    for h in range(nh):
+        K = O.rope_rotate(CK[h] @ BK[h], np.arange(L), base=50.0)
+        s = (K @ q[h]) / math.sqrt(H)
+        p = np.exp(s - s.max()); p /= p.sum()
+        assert np.allclose(got[0, h], p @ (CV[h] @ BV[h]), rtol=1e-12, atol=1e-12)
+    # one cached token sits at position 0: no rotation, same as the plain decode
+    inp1 = _inp_f64(q, CK[:, :1], CV[:, :1], BK, BV)
+    assert np.allclose(O.decode_attn_rope(inp1), O.decode_attn(inp1), atol=1e-12)
