@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fused low-rank decode attn: µs/step and achieved HBM GB/s (% of peak), 1 GPU"
 COLD_BYTES = 1 << 30      # rotate input copies until >= 1 GiB is touched
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["decode.hip", "wsvd_common.hpp"]
+KERNEL_SOURCES = ("decode.hip", "wsvd_common.hpp", "split_merge.hpp")
 
 
 def kernel_src_hash() -> str:

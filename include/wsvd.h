@@ -197,6 +197,48 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap,
                        hipStream_t stream);
 
 /*
+ * wsvd_decode_attn_rope -- wsvd_decode_attn with a rotary position step on
+ * every reconstructed key row.
+ *
+ * The pages' fused kernel rebuilds latent tiles through the head's factor
+ * on chip and uses them at once (German page section 2D, Italian page
+ * section 2D, Japanese page section 2.4, Arabic page section 2c); they name
+ * no position encoding.  With rotary embeddings the key of cached token t
+ * is R(t) (C_K[b,h,t,:] B_K[h]), which cannot be folded into q, so each key
+ * tile is rebuilt on matrix cores and rotated before the scores:
+ *
+ *     K_t = R(t) (C_K[b,h,t,:] B_K[h]),  V_t = C_V[b,h,t,:] B_V[h]
+ *     out[b,h,:] = softmax(sigma * K q[b,h,:]) V,   t = 0 .. L[b]-1
+ *
+ * R(t) rotates each pair (i, i + H/2) of a key by angle t * theta_i (the
+ * half-split convention); q must arrive already rotated to its own
+ * position.  cos / sin come from the tables below (row t, column i).
+ *
+ *   rope_cos, rope_sin  fp32 [L_cap, H/2], e.g. from wsvd_rope_tables
+ *   C_dt, B_dt          BF16 only; H in {64, 128}; r in {32, 64}
+ *   other arguments, the split rule, partials, workspace and merge exactly
+ *   as for wsvd_decode_attn (int8 caches are not supported here).
+ */
+int wsvd_decode_attn_rope(int nb, int nh, int H, int r, int L_cap,
+                          const int32_t* L,
+                          const void* q, wsvd_dtype q_dt,
+                          const void* C_K, const void* C_V, wsvd_dtype C_dt,
+                          const void* B_K, const void* B_V, wsvd_dtype B_dt,
+                          const float* rope_cos, const float* rope_sin,
+                          float softmax_scale, int n_splits,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, wsvd_dtype out_dt,
+                          hipStream_t stream);
+
+/*
+ * wsvd_rope_tables -- rope_cos[t, i] = cos(t * base^(-2 i / H)), rope_sin
+ * likewise, for t < L_cap and i < H/2 (fp32 [L_cap, H/2], computed in double
+ * and rounded once).  H even, base > 1 (e.g. 10000).
+ */
+int wsvd_rope_tables(int L_cap, int H, float base, float* rope_cos, float* rope_sin,
+                     hipStream_t stream);
+
+/*
  * W8A8 projection of the new token (German page section 2C, Italian page
  * section 2C, Japanese page section 2.3, Arabic page section 2c: the
  * low-rank layers run with 8-bit weights and activations, and an

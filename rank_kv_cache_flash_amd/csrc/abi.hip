@@ -189,6 +189,60 @@ int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap, const int32_t* L, c
     return wsvd::launch_dense_split(a, H, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
+int wsvd_rope_tables(int L_cap, int H, float base, float* rope_cos, float* rope_sin, hipStream_t stream) {
+    if (L_cap <= 0 || H <= 0 || H % 2 != 0 || !(base > 1.0f)) return WSVD_ERR_SHAPE;
+    if (!rope_cos || !rope_sin) return WSVD_ERR_NULL;
+    if ((long long)L_cap * H > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (!aligned16(rope_cos) || !aligned16(rope_sin)) return WSVD_ERR_ALIGN;
+    return wsvd::launch_rope_tables(L_cap, H, (double)base, rope_cos, rope_sin, stream) == hipSuccess ? WSVD_OK
+                                                                                                      : WSVD_ERR_HIP;
+}
+
+int wsvd_decode_attn_rope(int nb, int nh, int H, int r, int L_cap, const int32_t* L, const void* q,
+                          wsvd_dtype q_dt, const void* C_K, const void* C_V, wsvd_dtype C_dt, const void* B_K,
+                          const void* B_V, wsvd_dtype B_dt, const float* rope_cos, const float* rope_sin,
+                          float softmax_scale, int n_splits, void* workspace, size_t workspace_bytes, void* out,
+                          wsvd_dtype out_dt, hipStream_t stream) {
+    if (nb <= 0 || nh <= 0 || H <= 0 || r <= 0 || L_cap <= 0 || n_splits < 0 || r > H) return WSVD_ERR_SHAPE;
+    if ((long long)nb * nh * L_cap * r > (1ll << 46)) return WSVD_ERR_SHAPE;
+    if (!L || !q || !C_K || !C_V || !B_K || !B_V || !rope_cos || !rope_sin) return WSVD_ERR_NULL;
+    if (!act_dtype_ok(q_dt) || B_dt != WSVD_BF16 || C_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
+    if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
+    if (!head_dim_ok(H) || (r != 32 && r != 64)) return WSVD_ERR_UNSUPPORTED;
+    if (!aligned16(L) || !aligned16(q) || !aligned16(C_K) || !aligned16(C_V) || !aligned16(B_K) ||
+        !aligned16(B_V) || !aligned16(rope_cos) || !aligned16(rope_sin) || (out && !aligned16(out)))
+        return WSVD_ERR_ALIGN;
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0) return WSVD_ERR_SHAPE;
+    if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+
+    wsvd::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.nb = nb;
+    a.nh = nh;
+    a.L_cap = L_cap;
+    a.S = S;
+    a.L = L;
+    a.q = q;
+    a.q_dt = q_dt;
+    a.C_K = C_K;
+    a.C_V = C_V;
+    a.B_K = B_K;
+    a.B_V = B_V;
+    a.B_dt = B_dt;
+    const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
+    a.scale_log2 = sigma * wsvd::kLog2e;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
+    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                             wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits));
+    a.out = out;
+    a.out_dt = out ? (int)out_dt : 0;
+    return wsvd::launch_decode_rope(a, H, r, rope_cos, rope_sin, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
 int wsvd_combine_splits(int nb, int nh, int H, int n_splits, const float* o_part, const float* lse_part, void* out,
                         wsvd_dtype out_dt, hipStream_t stream) {
     if (nb <= 0 || nh <= 0 || H <= 0 || n_splits <= 0) return WSVD_ERR_SHAPE;

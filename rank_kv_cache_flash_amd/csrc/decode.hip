@@ -47,6 +47,7 @@
 // so each code costs one convert and one FMA.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
+#include "split_merge.hpp"
 
 namespace wsvd {
 
@@ -425,58 +426,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     if (tid == 0) store_coherent(a.lse_part + bh * S + s, lse_out);
 
     // ---- last split of (b, h) merges all partials ------------------------------
-    // The partials were stored write-through at device scope; once every wave
-    // has seen its stores complete, one relaxed device-scope increment
-    // publishes them.  The split that brings the count to S reads them back
-    // with device-scope loads (not served from a stale L2 line), so no
-    // cache-wide writeback or invalidate is needed.
     if (!a.out || S == 1) return;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-        sh_last = (__hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   (unsigned)(S - 1));
-    __syncthreads();
-    if (!sh_last) return;
-    // Online merge over chunks of up to 256 splits: one parallel load of the
-    // chunk's lse values into LDS, then each output lane issues its o_part
-    // loads eight at a time before consuming them.
-    const float* lsp = a.lse_part + bh * S;
-    const float* opp = a.o_part + bh * S * H;
-    float Mrun = kNegInf, accm = 0.f, wsum = 0.f;
-    for (int k0 = 0; k0 < S; k0 += 256) {
-        const int n = min(256, S - k0);
-        __syncthreads();
-        if (tid < n) sh_proj[tid] = load_coherent(lsp + k0 + tid);
-        __syncthreads();
-        float cm = kNegInf;
-        for (int k = 0; k < n; ++k) cm = fmaxf(cm, sh_proj[k]);
-        const float Mn = fmaxf(Mrun, cm);
-        if (Mn == kNegInf) continue;
-        const float rs = (Mrun == kNegInf) ? 0.f : fast_exp2((Mrun - Mn) * kLog2e);
-        accm *= rs;
-        wsum *= rs;
-        Mrun = Mn;
-        if (tid < H) {
-            for (int k = 0; k < n; k += 8) {
-                float ov[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    ov[u] = (k + u < n) ? load_coherent(opp + (size_t)(k0 + k + u) * H + tid) : 0.f;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    if (k + u < n) {
-                        const float lv = sh_proj[k + u];
-                        const float w = (lv == kNegInf) ? 0.f : fast_exp2((lv - Mn) * kLog2e);
-                        wsum += w;
-                        accm = fmaf(w, ov[u], accm);
-                    }
-                }
-            }
-        }
-    }
-    if (tid < H) store_elem_wt(a.out, a.out_dt, bh * H + tid, wsum > 0.f ? accm / wsum : 0.f);
-    if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_if_last_split<H>(a, bh, S, sh_proj, sh_last);
 }
 
 template <int H, int R, int CT, int BT>

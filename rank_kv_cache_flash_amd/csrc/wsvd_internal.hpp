@@ -31,6 +31,12 @@ struct DecodeArgs {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipStream_t st);
 
+// Decode with a rotary position step on every reconstructed key row
+// (bf16 caches and factors; H in 64, 128; r in 32, 64).
+hipError_t launch_decode_rope(const DecodeArgs& a, int H, int r, const float* rcos, const float* rsin,
+                              hipStream_t st);
+hipError_t launch_rope_tables(int L_cap, int H, double base, float* rcos, float* rsin, hipStream_t st);
+
 // Dense Flash-Decoding baseline (bf16 K / V rows of H values, no factors).
 hipError_t launch_dense_split(const DecodeArgs& a, int H, hipStream_t st);
 

@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
     L.wsvd_w8a8_quantize_activations.restype = i32
     L.wsvd_w8a8_prepare_factor.argtypes = [i32, i32, vp, i32, vp, vp, vp]
     L.wsvd_w8a8_prepare_factor.restype = i32
+    L.wsvd_decode_attn_rope.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp,
+                                        f32, i32, vp, sz, vp, i32, vp]
+    L.wsvd_decode_attn_rope.restype = i32
+    L.wsvd_rope_tables.argtypes = [i32, i32, f32, vp, vp, vp]
+    L.wsvd_rope_tables.restype = i32
     L.wsvd_decode_num_splits.argtypes = [i32, i32, i32, i32]
     L.wsvd_decode_num_splits.restype = i32
     L.wsvd_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -173,6 +178,67 @@ def decode_attn(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=N
     o_part = wsb[: nb * nh * S * H * 4].view(torch.float32).view(nb, nh, S, H)
     lse_part = wsb[off: off + nb * nh * S * 4].view(torch.float32).view(nb, nh, S)
     return out, o_part, lse_part
+
+
+def rope_tables(L_cap, H, base=10000.0, *, device="cuda", stream=None):
+    """wsvd_rope_tables: (cos, sin) fp32 [L_cap, H/2] of angle t * base^(-2 i / H)."""
+    c = torch.empty((L_cap, H // 2), dtype=torch.float32, device=device)
+    s_ = torch.empty_like(c)
+    _check(lib().wsvd_rope_tables(L_cap, H, float(base), _ptr(c), _ptr(s_), _stream(stream)), "wsvd_rope_tables")
+    return c, s_
+
+
+def _rope_args(q, C_K, C_V, B_K, B_V, L, rope_cos, rope_sin, softmax_scale, n_splits, workspace, out):
+    nb, nh, H = q.shape
+    L_cap, r = C_K.shape[2], C_K.shape[3]
+    return (nb, nh, H, r, L_cap, _ptr(L), _ptr(q), _DT[q.dtype], _ptr(C_K), _ptr(C_V), _DT[C_K.dtype], _ptr(B_K),
+            _ptr(B_V), _DT[B_K.dtype], _ptr(rope_cos), _ptr(rope_sin), float(softmax_scale or 0.0), int(n_splits or 0),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+            _DT[out.dtype] if out is not None else 0)
+
+
+def decode_attn_rope(q, C_K, C_V, B_K, B_V, L, rope_cos, rope_sin, *, softmax_scale=None, n_splits=None, out=None,
+                     out_dtype=None, workspace=None, partials_only=False, stream=None):
+    """wsvd_decode_attn_rope: as decode_attn, with keys rotated to their positions
+    (rope_cos / rope_sin fp32 [L_cap, H/2]); q is already rotated.  Returns
+    (out, o_part, lse_part) like decode_attn."""
+    for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"),
+                 (rope_cos, "rope_cos"), (rope_sin, "rope_sin"), (out, "out"), (workspace, "workspace")):
+        _dev(t, n)
+    nb, nh, H = q.shape
+    L_cap = C_K.shape[2]
+    S = decode_num_splits(nb, nh, L_cap, n_splits or 0)
+    if S <= 0:
+        raise WsvdError(S, "wsvd_decode_num_splits")
+    if workspace is None:
+        workspace = decode_workspace(nb, nh, H, L_cap, n_splits or 0, device=q.device)
+    if not partials_only and out is None:
+        out = torch.empty((nb, nh, H), dtype=out_dtype or q.dtype, device=q.device)
+    if partials_only:
+        out = None
+    st = lib().wsvd_decode_attn_rope(*_rope_args(q, C_K, C_V, B_K, B_V, L, rope_cos, rope_sin, softmax_scale,
+                                                 n_splits, workspace, out), _stream(stream))
+    _check(st, "wsvd_decode_attn_rope")
+    off = decode_lse_offset(nb, nh, H, L_cap, n_splits or 0)
+    wsb = workspace.view(torch.uint8).reshape(-1)
+    o_part = wsb[: nb * nh * S * H * 4].view(torch.float32).view(nb, nh, S, H)
+    lse_part = wsb[off: off + nb * nh * S * 4].view(torch.float32).view(nb, nh, S)
+    return out, o_part, lse_part
+
+
+class PreparedDecodeRope:
+    """wsvd_decode_attn_rope with fixed buffers; __call__(stream) enqueues it."""
+
+    def __init__(self, q, C_K, C_V, B_K, B_V, L, rope_cos, rope_sin, *, workspace, out=None, n_splits=None):
+        for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"),
+                     (rope_cos, "rope_cos"), (rope_sin, "rope_sin"), (out, "out"), (workspace, "workspace")):
+            _dev(t, n)
+        self._keep = (q, C_K, C_V, B_K, B_V, L, rope_cos, rope_sin, workspace, out)
+        self._args = _rope_args(q, C_K, C_V, B_K, B_V, L, rope_cos, rope_sin, None, n_splits, workspace, out)
+        self._fn = lib().wsvd_decode_attn_rope
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)), "wsvd_decode_attn_rope")
 
 
 def dense_decode_attn(q, K, V, L, *, softmax_scale=None, n_splits=None, out=None, out_dtype=None, workspace=None,

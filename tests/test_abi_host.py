@@ -208,3 +208,34 @@ def append_w8(L, **kw):
 ])
 def test_append_w8a8_rejects(L, kw, want):
     assert append_w8(L, **kw) == want
+
+
+def rope(L, **kw):
+    a = dict(nb=2, nh=4, H=128, r=32, L_cap=256, Lp=P, q=P, q_dt=BF16, C_K=P, C_V=P, C_dt=BF16, B_K=P, B_V=P,
+             B_dt=BF16, cos=P, sin=P, S=0, ws=P, ws_bytes=WS, out=P, out_dt=BF16)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return L.wsvd_decode_attn_rope(a["nb"], a["nh"], a["H"], a["r"], a["L_cap"], v(a["Lp"]), v(a["q"]), a["q_dt"],
+                                   v(a["C_K"]), v(a["C_V"]), a["C_dt"], v(a["B_K"]), v(a["B_V"]), a["B_dt"],
+                                   v(a["cos"]), v(a["sin"]), 0.0, a["S"], v(a["ws"]), a["ws_bytes"], v(a["out"]),
+                                   a["out_dt"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), ESHAPE), (dict(r=256), ESHAPE), (dict(cos=None), ENULL), (dict(sin=None), ENULL),
+    (dict(C_dt=I8), EDTYPE), (dict(B_dt=F32), EDTYPE), (dict(out_dt=I8), EDTYPE),
+    (dict(r=16), EUNSUP), (dict(r=48), EUNSUP), (dict(H=96), EUNSUP),
+    (dict(cos=P + 4), EALIGN), (dict(C_V=P + 2), EALIGN), ({}, EWS), (dict(ws=None), EWS),
+])
+def test_rope_rejects(L, kw, want):
+    assert rope(L, **kw) == want
+
+
+def test_rope_tables_rejects(L):
+    v = ctypes.c_void_p
+    f = L.wsvd_rope_tables
+    assert f(0, 128, 10000.0, v(P), v(P), None) == ESHAPE
+    assert f(16, 127, 10000.0, v(P), v(P), None) == ESHAPE
+    assert f(16, 128, 1.0, v(P), v(P), None) == ESHAPE
+    assert f(16, 128, 10000.0, None, v(P), None) == ENULL
+    assert f(16, 128, 10000.0, v(P), v(P + 4), None) == EALIGN
