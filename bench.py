@@ -213,6 +213,34 @@ def append_variants(cfg, steps, warmup=10, seed=0):
 
 
 # ---------------------------------------------------------------------------
+# rotary keys: rebuilt-key decode vs the folded decode on the same caches
+# ---------------------------------------------------------------------------
+def rope_vs_folded(w, steps, warmup=10):
+    """Time wsvd_decode_attn_rope on the workload's own buffers (with its
+    rotary tables) next to the folded wsvd_decode_attn already timed there.
+    Returns the per-step time and GB/s (same latent/factor/q/out bytes plus
+    the cos/sin tables once)."""
+    import torch
+    from rank_kv_cache_flash_amd import wsvd
+
+    cfg = w.cfg
+    if cfg.C_dt != "bf16" or cfg.r not in (32, 64) or cfg.H not in (64, 128):
+        return None
+    c, s_ = wsvd.rope_tables(cfg.L_cap, cfg.H)
+    calls = []
+    for d in w.sets:
+        out = torch.empty(cfg.nb, cfg.nh, cfg.H, dtype=d["q"].dtype, device="cuda")
+        ws = wsvd.decode_workspace(cfg.nb, cfg.nh, cfg.H, cfg.L_cap, 0)
+        calls.append(wsvd.PreparedDecodeRope(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], c, s_,
+                                             workspace=ws, out=out))
+    t = graph_time(lambda i: calls[i % len(calls)](), steps, warmup)[0]
+    nbytes = w.step_bytes + cfg.L_cap * cfg.H * 4
+    del calls
+    return {"us_per_step": round(t * 1e6, 3), "GB_per_s": round(nbytes / t / 1e9, 1),
+            "pct_of_hbm_peak": round(100.0 * nbytes / t / 1e9 / HBM_PEAK_GBS, 1)}
+
+
+# ---------------------------------------------------------------------------
 # dense Flash-Decoding baseline at the same shape (the pages' comparison)
 # ---------------------------------------------------------------------------
 def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
@@ -466,6 +494,8 @@ def main():
         torch.cuda.synchronize()
         cpu, parity = cpu_baseline(w, w.out, budget_s=args.cpu_budget)
 
+    rope_main = rope_vs_folded(w, args.steps, min(args.warmup, 10))
+
     vs_dense = None
     if not cfg.has_append and cfg.C_dt == "bf16":
         vs_dense = dense_vs_wsvd(cfg.nb, cfg.nh, cfg.H, cfg.r, cfg.L, args.steps, min(args.warmup, 10))
@@ -482,6 +512,9 @@ def main():
         wc, tsc, tdc = measure(c, k, min(args.warmup, 10))
         per[c.name] = summary(c, wc, tsc, tdc)
         per[c.name]["steps"] = k
+        rope = rope_vs_folded(wc, k, min(args.warmup, 10))
+        if rope is not None:
+            per[c.name]["rotary_keys"] = rope
         del wc
         torch.cuda.empty_cache()
         if c.has_append:
@@ -508,6 +541,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_max_rel_err_vs_oracle": parity,
         "vs_dense_flash_decoding": vs_dense,
+        "rotary_keys": rope_main,
         "per_config": per,
         "kernel_src": kernel_src_hash(),
     }

@@ -18,13 +18,15 @@
 //    in LDS.  The result (lane l: rows 4 (l / 16) .. +3, column l % 16 of
 //    each 16-column group) holds both members of every rotation pair
 //    (column c and c + H/2) in one lane.
-//  * Rotation: pair (c, c + H/2) of row t turns by t theta_c.  cos / sin at
-//    the lane's first row come from the caller's tables; the next three
-//    rows step by the angle-addition rule with (cos theta_c, sin theta_c)
-//    (table row 1).
-//  * Scores: the lane's columns times q (sigma log2 e folded in), summed
-//    over the 16 lanes of a DPP row; each lane then takes the score of its
-//    own A-operand row with one shuffle per row slot.
+//  * Rotation: pair (c, c + H/2) of row t turns by t theta_c.  Since
+//    <q, R(t) k> = <R(-t) q, k>, the lane turns its slice of q instead: to
+//    its first row's position with cos / sin from the caller's tables, then
+//    back by theta_c per following row (cos theta_c, sin theta_c are table
+//    row 1) -- four operations per pair and row instead of rotating the key
+//    and stepping the angle separately.
+//  * Scores: the lane's key columns times the turned q (sigma log2 e folded
+//    in), summed over the 16 lanes of a DPP row; each lane then takes the
+//    score of its own A-operand row with one shuffle per row slot.
 //  * Values stay in latent space: the lane accumulates p c_V of its row and
 //    rank chunk (online softmax per lane), and the split's r-vector is
 //    projected through B_Vh once, as in the folded kernel.
@@ -160,12 +162,13 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
                     kt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks].b, bf.b, kt[j], 0, 0, 0);
                 }
             }
-            // rotate rows 4 g + i (positions t0 + tb + 4 g + i) and dot with q
-            float cth[NP], sth[NP];
+            // rows 4 g + i sit at positions t0 + tb + 4 g + i: q turned back
+            // to the first of them, then back by one step per row
+            float q1[NP], q2[NP];
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                cth[p] = cr[p];
-                sth[p] = sr[p];
+                q1[p] = fmaf(qv[p], cr[p], qv[p + NP] * sr[p]);
+                q2[p] = fmaf(qv[p + NP], cr[p], -(qv[p] * sr[p]));
             }
             float sc[4];
 #pragma unroll
@@ -173,12 +176,13 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
                 float d = 0.f;
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
-                    const float x1 = kt[p][i], x2 = kt[p + NP][i];
-                    d = fmaf(x1 * cth[p] - x2 * sth[p], qv[p], d);
-                    d = fmaf(x2 * cth[p] + x1 * sth[p], qv[p + NP], d);
-                    const float cn = cth[p] * c1[p] - sth[p] * s1[p];
-                    sth[p] = sth[p] * c1[p] + cth[p] * s1[p];
-                    cth[p] = cn;
+                    d = fmaf(kt[p][i], q1[p], d);
+                    d = fmaf(kt[p + NP][i], q2[p], d);
+                    if (i < 3) {
+                        const float n1 = fmaf(q1[p], c1[p], q2[p] * s1[p]);
+                        q2[p] = fmaf(q2[p], c1[p], -(q1[p] * s1[p]));
+                        q1[p] = n1;
+                    }
                 }
                 d = group_sum<16>(d);
                 sc[i] = (tb + 4 * g + i < ntok) ? d : kNegInf;
@@ -189,21 +193,28 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
             const float y2 = __shfl(sc[2], src, 64), y3 = __shfl(sc[3], src, 64);
             const int q4 = rr & 3;
             const float my = q4 == 0 ? y0 : (q4 == 1 ? y1 : (q4 == 2 ? y2 : y3));
-            const float mn = fmaxf(m, my);
-            const float mu = (mn == kNegInf) ? 0.f : mn;
-            const float alpha = fast_exp2(m - mu);
-            const float pr = fast_exp2(my - mu);
-            l = l * alpha + pr;
+            // The running max moves only when some lane's score grows past it by
+            // more than 2^8 (or is first set): below that, exp2(score - m) stays
+            // under 256 and the accumulators need no rescaling.
+            if (__builtin_amdgcn_ballot_w64(my > m + 8.f)) {
+                const float mn = (my > m + 8.f) ? my : m;
+                const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
+                l *= alpha;
+#pragma unroll
+                for (int c = 0; c < 8 * KS; ++c) acc[c] *= alpha;
+                m = mn;
+            }
+            const float pr = fast_exp2(my - ((m == kNegInf) ? 0.f : m));
+            l += pr;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const uint32_t w = vr[ks].u[c >> 1];
                     const float vc = (c & 1) ? bf16_hi(w) : bf16_lo(w);
-                    acc[8 * ks + c] = fmaf(pr, vc, acc[8 * ks + c] * alpha);
+                    acc[8 * ks + c] = fmaf(pr, vc, acc[8 * ks + c]);
                 }
             }
-            m = mn;
         };
 
         const int nt = (ntok > tb0) ? (ntok - tb0 + STEP - 1) / STEP : 0;
