@@ -9,5 +9,7 @@ from .w8a8 import *  # noqa: F401,F403
 from .w8a8 import __all__ as _w8a8_all
 from .rope import *  # noqa: F401,F403
 from .rope import __all__ as _rope_all
+from .factorize import *  # noqa: F401,F403
+from .factorize import __all__ as _fact_all
 
-__all__ = list(_core_all) + list(_w8a8_all) + list(_rope_all)
+__all__ = list(_core_all) + list(_w8a8_all) + list(_rope_all) + list(_fact_all)

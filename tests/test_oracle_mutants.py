@@ -241,6 +241,41 @@ def _decode_rope_from_one(inp, base=10000.0, softmax_scale=None, pairs=None, _or
     return out
 
 
+def _svd_no_sigma(W, nh, r):
+    W = np.asarray(W, dtype=np.float64)
+    E, NH = W.shape
+    H = NH // nh
+    A = np.zeros((E, nh * r)); B = np.zeros((nh, r, H))
+    for h in range(nh):
+        U, s_, Vt = np.linalg.svd(W[:, h * H:(h + 1) * H], full_matrices=False)
+        A[:, h * r:(h + 1) * r] = U[:, :r]
+        B[h] = Vt[:r]
+    return A, B
+
+
+def _svd_smallest(W, nh, r):
+    W = np.asarray(W, dtype=np.float64)
+    E, NH = W.shape
+    H = NH // nh
+    A = np.zeros((E, nh * r)); B = np.zeros((nh, r, H))
+    for h in range(nh):
+        U, s_, Vt = np.linalg.svd(W[:, h * H:(h + 1) * H], full_matrices=False)
+        A[:, h * r:(h + 1) * r] = U[:, -r:] * s_[-r:]
+        B[h] = Vt[-r:]
+    return A, B
+
+
+def _als_A_unweighted(W, F, B, nh):
+    import oracle.factorize as Fm
+    return Fm.__dict__["_orig_als_step_A"](W, np.ones_like(np.asarray(F, np.float64)), B, nh)
+
+
+def _als_B_rows(W, F, A, nh):
+    import oracle.factorize as Fm
+    Fa = np.asarray(F, np.float64)
+    return Fm.__dict__["_orig_als_step_B"](W, Fa[::-1].copy(), A, nh)
+
+
 MUTANTS = {
     "softmax without max shift": ("softmax_weights", _softmax_nomax),
     "softmax sign flipped": ("softmax_weights", _softmax_sign),
@@ -271,6 +306,10 @@ MUTANTS = {
     "rope sine sign flipped": ("rope_rotate", _rope_sin_flipped),
     "rope frequency exponent halved": ("rope_angles", _rope_theta_half),
     "rope positions start at 1": ("decode_attn_rope", _decode_rope_from_one),
+    "svd latent without singular values": ("svd_factors", _svd_no_sigma),
+    "svd keeps the smallest directions": ("svd_factors", _svd_smallest),
+    "weighted A step ignores the weights": ("als_step_A", _als_A_unweighted),
+    "weighted B step uses the wrong rows of F": ("als_step_B", _als_B_rows),
 }
 
 
@@ -279,7 +318,10 @@ def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     import oracle.w8a8 as W8
     import oracle.rope as WR
-    for mod in (W, W8, WR, oracle):
+    import oracle.factorize as WF
+    WF.__dict__.setdefault("_orig_als_step_A", WF.als_step_A)
+    WF.__dict__.setdefault("_orig_als_step_B", WF.als_step_B)
+    for mod in (W, W8, WR, WF, oracle):
         if hasattr(mod, attr):
             monkeypatch.setattr(mod, attr, fn)
     caught = []

@@ -542,3 +542,65 @@ def test_rope_decode_one_token_and_brute_force():
     # one cached token sits at position 0: no rotation, same as the plain decode
     inp1 = _inp_f64(q, CK[:, :1], CV[:, :1], BK, BV)
     assert np.allclose(O.decode_attn_rope(inp1), O.decode_attn(inp1), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# offline per-head factorisation (truncated SVD; weighted alternating least squares)
+# ---------------------------------------------------------------------------
+def test_svd_factors_eckart_young():
+    rng = np.random.default_rng(41)
+    E, nh, H, r = 40, 2, 8, 3
+    W = rng.standard_normal((E, nh * H))
+    A, B = O.svd_factors(W, nh, r)
+    for h in range(nh):
+        Wh = W[:, h * H:(h + 1) * H]
+        err = np.sum((Wh - A[:, h * r:(h + 1) * r] @ B[h]) ** 2)
+        lam = np.sort(np.linalg.eigvalsh(Wh.T @ Wh))[::-1]       # squared singular values
+        assert np.isclose(err, lam[r:].sum(), rtol=1e-10)
+        assert np.allclose(B[h] @ B[h].T, np.eye(r), atol=1e-12)
+    A, B = O.svd_factors(W, nh, H)                               # full rank: exact
+    assert np.allclose(np.concatenate([A[:, h * H:(h + 1) * H] @ B[h] for h in range(nh)], axis=1), W, atol=1e-12)
+
+
+def test_svd_factors_hand_and_low_rank():
+    A, B = O.svd_factors(np.array([[3.0, 0.0], [0.0, 1.0], [0.0, 0.0]]), 1, 1)
+    assert np.allclose(A @ B[0], [[3.0, 0.0], [0.0, 0.0], [0.0, 0.0]], atol=1e-12)
+    rng = np.random.default_rng(42)
+    X, Y = rng.standard_normal((30, 4)), rng.standard_normal((4, 6))
+    A, B = O.svd_factors(X @ Y, 1, 4)
+    assert np.allclose(A @ B[0], X @ Y, atol=1e-10)
+
+
+def test_weighted_als_properties():
+    rng = np.random.default_rng(43)
+    E, nh, H, r = 24, 2, 6, 2
+    W = rng.standard_normal((E, nh * H))
+    F = rng.uniform(0.1, 3.0, (E, nh * H))
+    A, B = O.svd_factors(W, nh, r)
+    objs = [O.weighted_objective(W, F, A, B, nh)]
+    for _ in range(4):
+        A = O.als_step_A(W, F, B, nh)
+        objs.append(O.weighted_objective(W, F, A, B, nh))
+        # the A step is a minimiser: moving any row makes it worse
+        for _ in range(3):
+            D = np.zeros_like(A)
+            D[rng.integers(E), rng.integers(nh * r)] = 1e-3
+            assert np.all(O.weighted_objective(W, F, A + D, B, nh) >= objs[-1] - 1e-12)
+        B = O.als_step_B(W, F, A, nh)
+        objs.append(O.weighted_objective(W, F, A, B, nh))
+    objs = np.array(objs)
+    assert np.all(np.diff(objs, axis=0) <= 1e-12)              # never increases
+    # unit weights: the truncated SVD is a fixed point of the alternation
+    A0, B0 = O.svd_factors(W, nh, r)
+    A1, B1 = O.weighted_factors(W, np.ones_like(W), A0, B0, nh, 1)
+    for h in range(nh):
+        assert np.allclose(A1[:, h * r:(h + 1) * r] @ B1[h], A0[:, h * r:(h + 1) * r] @ B0[h], atol=1e-10)
+
+
+def test_weighted_als_recovers_low_rank():
+    rng = np.random.default_rng(44)
+    E, H, r = 30, 7, 2
+    W = rng.standard_normal((E, r)) @ rng.standard_normal((r, H))
+    F = rng.uniform(0.2, 5.0, (E, H))
+    A, B = O.weighted_factors(W, F, rng.standard_normal((E, r)), rng.standard_normal((1, r, H)), 1, 60)
+    assert O.weighted_objective(W, F, A, B, 1)[0] <= 1e-12 * np.sum(F * W * W)
