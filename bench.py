@@ -241,6 +241,64 @@ def rope_vs_folded(w, steps, warmup=10):
 
 
 # ---------------------------------------------------------------------------
+# offline per-head factorisation (run once per layer, not part of a step)
+# ---------------------------------------------------------------------------
+FP64_PEAK_TFLOPS = 78.6   # MI355X fp64 vector (and matrix) peak
+
+
+def factorize_offline(E=4096, nh=32, H=128, ranks=(32, 64), iters=5, cpu=True, seed=2900):
+    """Time wsvd_factorize_svd and the two weighted half-steps on one LLaVA-7B
+    projection (E 4096, 32 heads of 128) with eager launches, and the oracle
+    on a bounded sample of the same work.  fp64 flop counts: the Gram matrix
+    2 E H^2 per head (full square); each weighted solve 2 n r^2 to build its
+    normal matrix over n terms plus 2 r^3 for Gauss-Jordan."""
+    import numpy as np
+    import torch
+    from rank_kv_cache_flash_amd import inputs as I
+    from rank_kv_cache_flash_amd import wsvd
+
+    W = I.make_projection_weights(E, nh, H, seed=seed, spectrum="powerlaw")
+    F = I.make_fisher_weights(E, nh, H, seed=seed)
+    Wd = torch.from_numpy(W).cuda()
+    Fd = torch.from_numpy(F).cuda()
+    ws = torch.empty(wsvd.factorize_svd_workspace_bytes(E, nh, H), dtype=torch.uint8, device="cuda")
+    rec = {"shape": f"E={E} nh={nh} H={H}", "launch": "eager, inputs resident", "fp64_peak_TFLOPs": FP64_PEAK_TFLOPS}
+    for r in ranks:
+        A, B, sig, sw = wsvd.factorize_svd(Wd, nh, r, workspace=ws)
+        t_svd = eager_time(lambda i: wsvd.factorize_svd(Wd, nh, r, workspace=ws), iters, 2)
+        t_a = eager_time(lambda i: wsvd.weighted_update_A(Wd, Fd, B, out=A), iters, 2)
+        Bn = torch.empty_like(B)
+        t_b = eager_time(lambda i: wsvd.weighted_update_B(Wd, Fd, A, nh, out=Bn), iters, 2)
+        gram_flops = 2.0 * E * H * H * nh
+        fa = E * nh * (2.0 * H * r * r + 2.0 * r ** 3)
+        fb = nh * H * (2.0 * E * r * r + 2.0 * r ** 3)
+        row = {"svd_ms": round(t_svd * 1e3, 3), "svd_sweeps_max": int(sw.max().item()),
+               "svd_gram_TFLOPs_lower_bound": round(gram_flops / t_svd / 1e12, 2),
+               "weighted_A_ms": round(t_a * 1e3, 3), "weighted_A_TFLOPs": round(fa / t_a / 1e12, 2),
+               "weighted_B_ms": round(t_b * 1e3, 3), "weighted_B_TFLOPs": round(fb / t_b / 1e12, 2)}
+        if cpu:
+            import time
+            import oracle as O
+            hs = 2                                   # heads of the SVD sample
+            t0 = time.perf_counter()
+            O.svd_factors(W[:, :hs * H], hs, r)
+            t_osvd = (time.perf_counter() - t0) * nh / hs
+            rows = 64                                # rows of the A-step sample
+            t0 = time.perf_counter()
+            O.als_step_A(W[:rows], F[:rows], B.cpu().numpy().astype(np.float64), nh)
+            t_oa = (time.perf_counter() - t0) * E / rows
+            t0 = time.perf_counter()                 # one head of the B step
+            O.als_step_B(W[:, :H], F[:, :H], A[:, :r].cpu().numpy().astype(np.float64), 1)
+            t_ob = (time.perf_counter() - t0) * nh
+            row["oracle_cpu"] = {"svd_ms": round(t_osvd * 1e3, 1), "weighted_A_ms": round(t_oa * 1e3, 1),
+                                 "weighted_B_ms": round(t_ob * 1e3, 1), "cores": torch.get_num_threads(),
+                                 "sample": f"SVD of {hs} heads x{nh // hs}; A step on {rows} rows x{E // rows}; "
+                                           f"B step on 1 head x{nh}"}
+        rec[f"r={r}"] = row
+    return rec
+
+
+# ---------------------------------------------------------------------------
 # dense Flash-Decoding baseline at the same shape (the pages' comparison)
 # ---------------------------------------------------------------------------
 def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
@@ -393,11 +451,14 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep"],
+    ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep",
+                                       "factorize-loop"],
                     default="bench",
                     help="decode-loop / step-loop / copy-calib / counters: plain launch loops for traces and counters")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--no-factorize", dest="factorize", action="store_false",
+                    help="skip timing the offline per-head factorisation")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -462,6 +523,20 @@ def main():
             torch.cuda.empty_cache()
         print(json.dumps(rec))
         return
+    if args.mode == "factorize-loop":
+        # Plain launch loop for kernel traces: per-head SVD at rank 32, then
+        # one weighted A and B half-step, repeated.
+        from rank_kv_cache_flash_amd import inputs as I
+        E, nh, H, r = 4096, 32, 128, 32
+        Wd = torch.from_numpy(I.make_projection_weights(E, nh, H, seed=2900, spectrum="powerlaw")).cuda()
+        Fd = torch.from_numpy(I.make_fisher_weights(E, nh, H, seed=2900)).cuda()
+        for _ in range(args.steps):
+            A, B, _, _ = wsvd.factorize_svd(Wd, nh, r)
+            wsvd.weighted_update_A(Wd, Fd, B, out=A)
+            wsvd.weighted_update_B(Wd, Fd, A, nh, out=B)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": args.mode, "shape": f"E={E} nh={nh} H={H} r={r}", "launches": args.steps}))
+        return
     if args.mode in ("decode-loop", "step-loop"):
         # Plain launch loops (no graph) for kernel traces: the split kernel
         # alone (partials only, as timed for the roofline) or whole steps.
@@ -520,6 +595,11 @@ def main():
         if c.has_append:
             per[c.name]["append_alone"] = append_variants(c, max(k, 100), min(args.warmup, 10))
 
+    offline = None
+    if args.factorize:
+        offline = factorize_offline(cpu=not args.no_cpu)
+        torch.cuda.empty_cache()
+
     line = {
         "metric": METRIC,
         "value": round(w_bytes_gbs(main_sum), 1),
@@ -543,6 +623,7 @@ def main():
         "vs_dense_flash_decoding": vs_dense,
         "rotary_keys": rope_main,
         "per_config": per,
+        "offline_factorize": offline,
         "kernel_src": kernel_src_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -331,6 +331,61 @@ size_t wsvd_decode_counter_offset(int nb, int nh, int H, int L_cap, int n_splits
  * Pure host. */
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r);
 
+/*
+ * Offline per-head factorisation (Arabic page section 2a, German page
+ * section 2A, Japanese page section 2.1: every head's E x H slice W_h of a
+ * projection is factored on its own at rank r, W_h ~ A_h B_h).  Readings:
+ * W fp32 [E, nh*H] holds the heads side by side (columns [h H, (h + 1) H)
+ * are W_h); the unweighted factors are the rank-r truncated SVD W_h =
+ * U S V^T, split as A_h = U_r S_r and B_h = V_r^T, so the latent keeps the
+ * singular values and the rows of B_h are orthonormal.  Offline work: run
+ * once per layer, nothing here is on the decode path.
+ *
+ * wsvd_factorize_svd -- A fp32 [E, nh*r] (column block h is A_h), B fp32
+ * [nh, r, H] (B_h = B[h]), sigma fp32 [nh, H] (all H singular values of
+ * each head, descending), sweeps int32 [nh] or NULL (Jacobi sweeps used per
+ * head, negative when the iteration stopped at its cap without converging).
+ * Computed in fp64 through G_h = W_h^T W_h (its eigenvectors are the right
+ * singular vectors); rows of B_h are orthonormal with their largest-
+ * magnitude entry positive; where W_h has rank below r the missing rows
+ * complete an orthonormal set (their A columns are then zero to rounding).
+ * A_h = W_h B_h^T with the returned fp32 B.  H in {64, 128}; 1 <= r <= H.
+ * Workspace: wsvd_factorize_svd_workspace_bytes(E, nh, H) bytes, 16-byte
+ * aligned, no initial contents required.  Non-finite W gives non-finite
+ * outputs.
+ */
+size_t wsvd_factorize_svd_workspace_bytes(int E, int nh, int H);
+int wsvd_factorize_svd(int E, int nh, int H, int r, const float* W,
+                       float* A, float* B, float* sigma, int32_t* sweeps,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * Weighted refinement (Arabic page section 2b, German page section 2B,
+ * Japanese page section 2.2: factors are fitted to minimise
+ * sum F (.) (W - A B)^2 with importance weights F).  Reading: alternating
+ * least squares with F given (fp32 [E, nh*H], laid out like W, entries > 0
+ * and finite); each call is one exact half-step, solved in fp64:
+ *
+ * wsvd_weighted_update_A -- every row a of A_h (output fp32 [E, nh*r])
+ *   minimises sum_j F[e, hH + j] (W[e, hH + j] - a . B_h[:, j])^2 for the
+ *   given B fp32 [nh, r, H];
+ * wsvd_weighted_update_B -- every column b of B_h (output fp32 [nh, r, H])
+ *   minimises sum_e F[e, hH + j] (W[e, hH + j] - A_h[e, :] . b)^2 for the
+ *   given A fp32 [E, nh*r].
+ *
+ * H in {64, 128}; r in {16, 32, 48, 64}.  The r x r normal matrix of every
+ * row (column) must be positive definite (B_h of full row rank, A_h of full
+ * column rank over the rows with weight); a singular one yields non-finite
+ * values in that row (column).  No workspace.
+ */
+int wsvd_weighted_update_A(int E, int nh, int H, int r, const float* W,
+                           const float* F, const float* B, float* A,
+                           hipStream_t stream);
+int wsvd_weighted_update_B(int E, int nh, int H, int r, const float* W,
+                           const float* F, const float* A, float* B,
+                           hipStream_t stream);
+
 /* Static description of a status code.  Pure host; never NULL. */
 const char* wsvd_status_string(int status);
 

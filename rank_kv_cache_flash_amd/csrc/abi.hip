@@ -366,4 +366,51 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
+size_t wsvd_factorize_svd_workspace_bytes(int E, int nh, int H) {
+    if (E <= 0 || nh <= 0 || !head_dim_ok(H)) return 0;
+    return (size_t)wsvd::svd_num_chunks(E, nh) * nh * H * H * sizeof(double);
+}
+
+int wsvd_factorize_svd(int E, int nh, int H, int r, const float* W, float* A, float* B, float* sigma, int* sweeps,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (E <= 0 || nh <= 0 || r <= 0 || H <= 0 || r > H) return WSVD_ERR_SHAPE;
+    if (nh > 65535 || (long long)E * nh * H > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (!head_dim_ok(H)) return WSVD_ERR_UNSUPPORTED;
+    if (!W || !A || !B || !sigma) return WSVD_ERR_NULL;
+    if (!aligned16(W) || !aligned16(A) || !aligned16(B) || !aligned16(sigma)) return WSVD_ERR_ALIGN;
+    const size_t need = wsvd_factorize_svd_workspace_bytes(E, nh, H);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+    return wsvd::launch_factorize_svd(W, E, nh, H, r, A, B, sigma, sweeps, static_cast<double*>(workspace), stream) ==
+                   hipSuccess
+               ? WSVD_OK
+               : WSVD_ERR_HIP;
+}
+
+static int check_weighted(int E, int nh, int H, int r, const float* W, const float* F, const float* in,
+                          const float* out) {
+    if (E <= 0 || nh <= 0 || r <= 0 || H <= 0 || r > H) return WSVD_ERR_SHAPE;
+    if (nh > 65535 || (long long)E * nh * H > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (!head_dim_ok(H) || !rank_ok(r)) return WSVD_ERR_UNSUPPORTED;
+    if (!W || !F || !in || !out) return WSVD_ERR_NULL;
+    if (!aligned16(W) || !aligned16(F) || !aligned16(in) || !aligned16(out)) return WSVD_ERR_ALIGN;
+    return WSVD_OK;
+}
+
+int wsvd_weighted_update_A(int E, int nh, int H, int r, const float* W, const float* F, const float* B, float* A,
+                           hipStream_t stream) {
+    const int st = check_weighted(E, nh, H, r, W, F, B, A);
+    if (st != WSVD_OK) return st;
+    return wsvd::launch_factorize_weighted(true, W, F, B, E, nh, H, r, A, stream) == hipSuccess ? WSVD_OK
+                                                                                               : WSVD_ERR_HIP;
+}
+
+int wsvd_weighted_update_B(int E, int nh, int H, int r, const float* W, const float* F, const float* A, float* B,
+                           hipStream_t stream) {
+    const int st = check_weighted(E, nh, H, r, W, F, A, B);
+    if (st != WSVD_OK) return st;
+    return wsvd::launch_factorize_weighted(false, W, F, A, E, nh, H, r, B, stream) == hipSuccess ? WSVD_OK
+                                                                                                : WSVD_ERR_HIP;
+}
+
 }  // extern "C"
+

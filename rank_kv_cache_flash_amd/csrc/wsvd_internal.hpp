@@ -81,4 +81,14 @@ long append_num_tiles(int nb, int nh, int r);
 // Bytes of split-E partial tiles for these sizes, 0 when KS == 1 (host).
 size_t append_partial_bytes(int nb, int E, int nh, int r);
 
+// Offline per-head factorisation (factorize.hip).  Truncated SVD: Gram
+// partials into Gpart ([chunks, nh, H, H] fp64), Jacobi per head, then
+// A = W B^T.  Weighted refinement: one alternating least squares half-step,
+// rows = true solves the rows of A from B, false the columns of B from A.
+int svd_num_chunks(int E, int nh);
+hipError_t launch_factorize_svd(const float* W, int E, int nh, int H, int r, float* A, float* B, float* sigma,
+                                int* sweeps, double* Gpart, hipStream_t st);
+hipError_t launch_factorize_weighted(bool rows, const float* W, const float* F, const float* in, int E, int nh,
+                                     int H, int r, float* out, hipStream_t st);
+
 }  // namespace wsvd

@@ -226,3 +226,42 @@ def make_w8a8_codes(nb, E, N, *, seed):
     sx = (np.exp2(_rng(seed, T_SX).uniform(-12, -8, size=nb))).astype(np.float32)
     sA = (np.exp2(_rng(seed, T_SA).uniform(-10, -6, size=N))).astype(np.float32)
     return xq, sx, AqT, sA
+
+
+T_WP, T_WU, T_WV, T_WS, T_F = range(30, 35)
+
+
+def make_projection_weights(E, nh, H, *, seed, spectrum="gaussian", rank=None):
+    """A projection W fp32 [E, nh*H] whose column block h is head h's slice.
+
+    spectrum = "gaussian": i.i.d. N(0, 1)/sqrt(E) entries (singular values
+    packed in a Marchenko-Pastur band); "powerlaw": W_h = U diag(s) V^T with
+    Haar-random orthonormal U [E, k], V [H, k], k = min(E, H) (QR of Gaussian
+    draws, signs fixed by the diagonal of R) and s_i = (i + 1)^(-1/2), a smoothly decaying
+    spectrum with distinct values; "lowrank": (E x rank) @ (rank x H)
+    Gaussian product, so W_h has rank `rank` exactly."""
+    W = np.zeros((E, nh * H), np.float32)
+    for h in range(nh):
+        if spectrum == "gaussian":
+            Wh = _rng(seed, T_WP, h).standard_normal((E, H)) / np.sqrt(E)
+        elif spectrum == "powerlaw":
+            def haar(key, m, n):
+                Q, R = np.linalg.qr(_rng(seed, key, h).standard_normal((m, n)))
+                return Q * np.sign(np.diag(R))
+            k = min(E, H)
+            s = (np.arange(k) + 1.0) ** -0.5
+            Wh = (haar(T_WU, E, k) * s) @ haar(T_WV, H, k).T
+        elif spectrum == "lowrank":
+            g = _rng(seed, T_WS, h)
+            Wh = g.standard_normal((E, rank)) @ g.standard_normal((rank, H)) / np.sqrt(E * rank)
+        else:
+            raise ValueError(spectrum)
+        W[:, h * H:(h + 1) * H] = Wh
+    return W
+
+
+def make_fisher_weights(E, nh, H, *, seed, sigma=1.0):
+    """Importance weights F fp32 [E, nh*H], laid out like W: log-normal,
+    exp(N(0, sigma^2)), positive with a heavy upper tail (diagonal Fisher
+    information is a mean of squared gradients)."""
+    return np.exp(sigma * _rng(seed, T_F).standard_normal((E, nh * H))).astype(np.float32)

@@ -68,6 +68,14 @@ def lib() -> ctypes.CDLL:
     L.wsvd_decode_counter_offset.restype = sz
     L.wsvd_append_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.wsvd_append_workspace_bytes.restype = sz
+    L.wsvd_factorize_svd_workspace_bytes.argtypes = [i32, i32, i32]
+    L.wsvd_factorize_svd_workspace_bytes.restype = sz
+    L.wsvd_factorize_svd.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.wsvd_factorize_svd.restype = i32
+    L.wsvd_weighted_update_A.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.wsvd_weighted_update_A.restype = i32
+    L.wsvd_weighted_update_B.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.wsvd_weighted_update_B.restype = i32
     L.wsvd_status_string.argtypes = [i32]
     L.wsvd_status_string.restype = ctypes.c_char_p
     L.wsvd_version.argtypes = []
@@ -353,6 +361,64 @@ def append_latent_w8a8(xq, sx, AqT_K, sA_K, AqT_V, sA_V, pos, C_K, C_V, *, s_K=N
 # ---------------------------------------------------------------------------
 # host arrays (storage dtypes from rank_kv_cache_flash_amd.inputs) -> device
 # ---------------------------------------------------------------------------
+def _f32(t, name):
+    _dev(t, name)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+
+
+def factorize_svd_workspace_bytes(E, nh, H) -> int:
+    return int(lib().wsvd_factorize_svd_workspace_bytes(E, nh, H))
+
+
+def factorize_svd(W, nh, r, *, workspace=None, stream=None):
+    """wsvd_factorize_svd: W fp32 [E, nh*H] -> (A [E, nh*r], B [nh, r, H],
+    sigma [nh, H], sweeps int32 [nh]), the per-head rank-r truncated SVD."""
+    _f32(W, "W")
+    E, NH = W.shape
+    H = NH // nh
+    dev = W.device
+    A = torch.empty((E, nh * r), dtype=torch.float32, device=dev)
+    B = torch.empty((nh, r, H), dtype=torch.float32, device=dev)
+    sigma = torch.empty((nh, H), dtype=torch.float32, device=dev)
+    sweeps = torch.empty((nh,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(factorize_svd_workspace_bytes(E, nh, H), 256), dtype=torch.uint8, device=dev)
+    _check(lib().wsvd_factorize_svd(E, nh, H, r, _ptr(W), _ptr(A), _ptr(B), _ptr(sigma), _ptr(sweeps),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "wsvd_factorize_svd")
+    return A, B, sigma, sweeps
+
+
+def weighted_update_A(W, F, B, *, out=None, stream=None):
+    """wsvd_weighted_update_A: rows of A [E, nh*r] minimising the F-weighted
+    error against W for the given B [nh, r, H]."""
+    for t, n in ((W, "W"), (F, "F"), (B, "B")):
+        _f32(t, n)
+    nh, r, H = B.shape
+    E = W.shape[0]
+    A = torch.empty((E, nh * r), dtype=torch.float32, device=W.device) if out is None else out
+    _f32(A, "out")
+    _check(lib().wsvd_weighted_update_A(E, nh, H, r, _ptr(W), _ptr(F), _ptr(B), _ptr(A), _stream(stream)),
+           "wsvd_weighted_update_A")
+    return A
+
+
+def weighted_update_B(W, F, A, nh, *, out=None, stream=None):
+    """wsvd_weighted_update_B: columns of B [nh, r, H] minimising the
+    F-weighted error against W for the given A [E, nh*r]."""
+    for t, n in ((W, "W"), (F, "F"), (A, "A")):
+        _f32(t, n)
+    E, NH = W.shape
+    H = NH // nh
+    r = A.shape[1] // nh
+    B = torch.empty((nh, r, H), dtype=torch.float32, device=W.device) if out is None else out
+    _f32(B, "out")
+    _check(lib().wsvd_weighted_update_B(E, nh, H, r, _ptr(W), _ptr(F), _ptr(A), _ptr(B), _stream(stream)),
+           "wsvd_weighted_update_B")
+    return B
+
+
 def to_device(arr, dt: str, device="cuda"):
     """NumPy array in a storage dtype ('f32', 'bf16' bits, 'f16', 'i8', int32) -> GPU tensor."""
     import numpy as np

@@ -239,3 +239,44 @@ def test_rope_tables_rejects(L):
     assert f(16, 128, 1.0, v(P), v(P), None) == ESHAPE
     assert f(16, 128, 10000.0, None, v(P), None) == ENULL
     assert f(16, 128, 10000.0, v(P), v(P + 4), None) == EALIGN
+
+
+def svd(L, E=512, nh=4, H=128, r=32, W=P, A=P, B=P, sigma=P, sweeps=None, ws=P, ws_bytes=16):
+    v = ctypes.c_void_p
+    return L.wsvd_factorize_svd(E, nh, H, r, v(W) if W else None, v(A) if A else None, v(B) if B else None,
+                                v(sigma) if sigma else None, v(sweeps) if sweeps else None, v(ws) if ws else None,
+                                ws_bytes, None)
+
+
+def test_factorize_svd_workspace_size(L):
+    f = wsvd.factorize_svd_workspace_bytes
+    for E, nh, H in [(4096, 32, 128), (100, 1, 64), (4096, 1, 128), (33, 700, 64)]:
+        n = f(E, nh, H)
+        chunks = n // (nh * H * H * 8)
+        assert n == chunks * nh * H * H * 8 and 1 <= chunks <= max(1, (E + 63) // 64)
+    assert f(0, 4, 128) == 0 and f(16, 4, 96) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(E=0), ESHAPE), (dict(nh=0), ESHAPE), (dict(r=0), ESHAPE), (dict(r=129), ESHAPE),
+    (dict(nh=70000), ESHAPE), (dict(H=96, r=32), EUNSUP), (dict(W=None), ENULL), (dict(A=None), ENULL),
+    (dict(B=None), ENULL), (dict(sigma=None), ENULL), (dict(W=P + 4), EALIGN), (dict(sigma=P + 8), EALIGN),
+    ({}, EWS), (dict(ws=None, ws_bytes=1 << 40), EWS), (dict(ws=P + 4, ws_bytes=1 << 40), EWS),
+])
+def test_factorize_svd_rejects(L, kw, want):
+    assert svd(L, **kw) == want
+
+
+@pytest.mark.parametrize("fn", ["wsvd_weighted_update_A", "wsvd_weighted_update_B"])
+@pytest.mark.parametrize("args,want", [
+    ((0, 4, 128, 32, P, P, P, P), ESHAPE), ((64, 4, 128, 0, P, P, P, P), ESHAPE),
+    ((64, 4, 64, 128, P, P, P, P), ESHAPE), ((64, 4, 96, 32, P, P, P, P), EUNSUP),
+    ((64, 4, 128, 40, P, P, P, P), EUNSUP), ((64, 4, 128, 32, None, P, P, P), ENULL),
+    ((64, 4, 128, 32, P, None, P, P), ENULL), ((64, 4, 128, 32, P, P, None, P), ENULL),
+    ((64, 4, 128, 32, P, P, P, None), ENULL), ((64, 4, 128, 32, P, P + 4, P, P), EALIGN),
+    ((64, 4, 128, 32, P, P, P, P + 12), EALIGN),
+])
+def test_weighted_update_rejects(L, fn, args, want):
+    v = ctypes.c_void_p
+    conv = [a if i < 4 else (v(a) if a else None) for i, a in enumerate(args)]
+    assert getattr(L, fn)(*conv, None) == want
