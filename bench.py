@@ -279,11 +279,11 @@ def factorize_offline(E=4096, nh=32, H=128, ranks=(32, 64), iters=5, cpu=True, s
         if cpu:
             import time
             import oracle as O
-            hs = 2                                   # heads of the SVD sample
+            hs = 1                                   # heads of the SVD sample
             t0 = time.perf_counter()
             O.svd_factors(W[:, :hs * H], hs, r)
             t_osvd = (time.perf_counter() - t0) * nh / hs
-            rows = 64                                # rows of the A-step sample
+            rows = 16                                # rows of the A-step sample
             t0 = time.perf_counter()
             O.als_step_A(W[:rows], F[:rows], B.cpu().numpy().astype(np.float64), nh)
             t_oa = (time.perf_counter() - t0) * E / rows
