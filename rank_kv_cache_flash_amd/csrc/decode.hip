@@ -191,33 +191,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int b = rest / a.S;
     const int S = a.S;
 
+    const size_t bh = (size_t)b * a.nh + h;
     int ell = a.L[b];
+
+    // ---- requests: q, B_K, B_V (independent of the length, so they travel
+    // together with the L[b] read instead of after it) ----------------------
+    const size_t q_idx = bh * H + (tid < H ? tid : 0);
+    const uint32_t q_word = load_q_word(a.q, a.q_dt, q_idx);
+    const char* bk_base = static_cast<const char*>(a.B_K) + (size_t)h * R * H * BES;
+    const char* bv_base = static_cast<const char*>(a.B_V) + (size_t)h * R * H * BES;
+    u32x4 bk[NBT], bv[NBT];
+#pragma unroll
+    for (int k = 0; k < NBT; ++k) {
+        const int c = tid + 256 * k;
+        if (!DENSE && (NBC % 256 == 0 || c < NBC)) {
+            bk[k] = *reinterpret_cast<const u32x4*>(bk_base + (size_t)c * 16);
+            bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
+        }
+    }
+
     ell = min(max(ell, 0), a.L_cap);
     const int chunk = (ell + S - 1) / S;
     const int t0 = min(ell, s * chunk);
     const int t1 = min(ell, t0 + chunk);
     const int ntok = t1 - t0;
 
-    const size_t bh = (size_t)b * a.nh + h;
     float* o_out = a.o_part + (bh * S + s) * H;
     float lse_out = kNegInf;
 
-    if (ntok > 0) {  // uniform over the block
-        // ---- requests: q, B_K, B_V, first latent batches ----------------------
-        const size_t q_idx = bh * H + (tid < H ? tid : 0);
-        const uint32_t q_word = load_q_word(a.q, a.q_dt, q_idx);
-        const char* bk_base = static_cast<const char*>(a.B_K) + (size_t)h * R * H * BES;
-        const char* bv_base = static_cast<const char*>(a.B_V) + (size_t)h * R * H * BES;
-        u32x4 bk[NBT], bv[NBT];
-#pragma unroll
-        for (int k = 0; k < NBT; ++k) {
-            const int c = tid + 256 * k;
-            if (!DENSE && (NBC % 256 == 0 || c < NBC)) {
-                bk[k] = *reinterpret_cast<const u32x4*>(bk_base + (size_t)c * 16);
-                bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
-            }
-        }
-
+    // No branch on ntok: every block runs the same code, so nothing keeps the
+    // factor and q requests above from being issued before L[b] lands.  An
+    // empty range (ntok == 0) requests no latent tile and ends with a zero
+    // partial and lse = -inf.
+    {
+        // ---- first latent batches ---------------------------------------------
         const int g = lane / GP;
         const int j = lane % GP;
         const bool act = j < G;
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             float o = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) o = fmaf(sh_red_o[w][tid], wt[w], o);
-            sh_on[tid] = o / Lt;
+            sh_on[tid] = Lt > 0.f ? o / Lt : 0.f;
         }
         __syncthreads();
         if constexpr (!DENSE) {
@@ -416,12 +423,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             store_coherent(o_out + tid, o);
             if (S == 1 && a.out) store_elem_wt(a.out, a.out_dt, bh * H + tid, o);
         }
-        lse_out = (M + fast_log2(Lt)) * kLn2;
-    } else {
-        for (int i = tid; i < H; i += 256) {
-            store_coherent(o_out + i, 0.f);
-            if (S == 1 && a.out) store_elem_wt(a.out, a.out_dt, bh * H + i, 0.f);
-        }
+        lse_out = Lt > 0.f ? (M + fast_log2(Lt)) * kLn2 : kNegInf;
     }
     if (tid == 0) store_coherent(a.lse_part + bh * S + s, lse_out);
 
