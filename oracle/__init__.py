@@ -11,5 +11,7 @@ from .rope import *  # noqa: F401,F403
 from .rope import __all__ as _rope_all
 from .factorize import *  # noqa: F401,F403
 from .factorize import __all__ as _fact_all
+from .shared_svd import *  # noqa: F401,F403
+from .shared_svd import __all__ as _shared_all
 
-__all__ = list(_core_all) + list(_w8a8_all) + list(_rope_all) + list(_fact_all)
+__all__ = list(_core_all) + list(_w8a8_all) + list(_rope_all) + list(_fact_all) + list(_shared_all)

@@ -265,3 +265,47 @@ def make_fisher_weights(E, nh, H, *, seed, sigma=1.0):
     exp(N(0, sigma^2)), positive with a heavy upper tail (diagonal Fisher
     information is a mean of squared gradients)."""
     return np.exp(sigma * _rng(seed, T_F).standard_normal((E, nh * H))).astype(np.float32)
+
+
+T_SQ, T_SCK, T_SCV, T_SBK, T_SBV = range(40, 45)
+
+
+@dataclass
+class SharedInputs:
+    """One decode step of the conventional (whole-matrix) factorisation: a
+    latent of rank R shared by all heads, and factors B [R, nh*H] whose
+    column block h maps it to head h's keys (values)."""
+    nb: int
+    nh: int
+    H: int
+    R: int
+    L_cap: int
+    q: np.ndarray            # [nb, nh, H]
+    C_K: np.ndarray          # [nb, L_cap, R]
+    C_V: np.ndarray
+    B_K: np.ndarray          # [R, nh*H]
+    B_V: np.ndarray
+    L: np.ndarray            # int32 [nb]
+    dt: str = "bf16"         # storage dtype of every tensor above except L
+
+
+def make_shared_inputs(nb, nh, H, R, L, L_cap, *, seed, dt="bf16", q_gain=1.0) -> SharedInputs:
+    """Draw a shared-latent decode step: latents N(0, 1)/sqrt(R), factors
+    N(0, 1)/sqrt(H), q N(0, 1) q_gain/sqrt(H), so a reconstructed key has
+    the per-entry variance (1/H) of the per-head workloads.  Cache rows at or
+    beyond L[b] are zero."""
+    L = np.broadcast_to(np.asarray(L, dtype=np.int32), (nb,)).copy()
+    q = np.stack([_normal(seed, (T_SQ, b), (nh, H), q_gain / np.sqrt(H)) for b in range(nb)])
+
+    def lat(tid):
+        out = np.zeros((nb, L_cap, R), np.float32)
+        for b in range(nb):
+            n = int(min(max(L[b], 0), L_cap))
+            out[b, :n] = _normal(seed, (tid, b), (n, R), 1.0 / np.sqrt(R))
+        return out
+
+    C_K, C_V = lat(T_SCK), lat(T_SCV)
+    B_K = _normal(seed, (T_SBK,), (R, nh * H), 1.0 / np.sqrt(H))
+    B_V = _normal(seed, (T_SBV,), (R, nh * H), 1.0 / np.sqrt(H))
+    return SharedInputs(nb=nb, nh=nh, H=H, R=R, L_cap=L_cap, q=_store(q, dt), C_K=_store(C_K, dt),
+                        C_V=_store(C_V, dt), B_K=_store(B_K, dt), B_V=_store(B_V, dt), L=L, dt=dt)

@@ -276,6 +276,25 @@ def _als_B_rows(W, F, A, nh):
     return Fm.__dict__["_orig_als_step_B"](W, Fa[::-1].copy(), A, nh)
 
 
+def _shared_one_next_head(inp, b, h, softmax_scale=None):
+    import oracle.shared_svd as S
+    return S.__dict__["_orig_one"](inp, b, (h + 1) % inp.nh, softmax_scale)
+
+
+def _shared_one_v_with_k_factor(inp, b, h, softmax_scale=None):
+    import dataclasses
+    import oracle.shared_svd as S
+    return S.__dict__["_orig_one"](dataclasses.replace(inp, B_V=inp.B_K), b, h, softmax_scale)
+
+
+def _shared_one_wrong_sequence(inp, b, h, softmax_scale=None):
+    import dataclasses
+    import oracle.shared_svd as S
+    bb = (b + 1) % inp.nb
+    sub = dataclasses.replace(inp, C_K=inp.C_K[[bb] * inp.nb], C_V=inp.C_V[[bb] * inp.nb])
+    return S.__dict__["_orig_one"](sub, b, h, softmax_scale)
+
+
 MUTANTS = {
     "softmax without max shift": ("softmax_weights", _softmax_nomax),
     "softmax sign flipped": ("softmax_weights", _softmax_sign),
@@ -310,6 +329,9 @@ MUTANTS = {
     "svd keeps the smallest directions": ("svd_factors", _svd_smallest),
     "weighted A step ignores the weights": ("als_step_A", _als_A_unweighted),
     "weighted B step uses the wrong rows of F": ("als_step_B", _als_B_rows),
+    "shared factor column block of the next head": ("decode_attn_shared_one", _shared_one_next_head),
+    "shared values rebuilt with the key factor": ("decode_attn_shared_one", _shared_one_v_with_k_factor),
+    "shared latent of the next sequence": ("decode_attn_shared_one", _shared_one_wrong_sequence),
 }
 
 
@@ -321,7 +343,9 @@ def test_pins_catch_mutant(name, monkeypatch):
     import oracle.factorize as WF
     WF.__dict__.setdefault("_orig_als_step_A", WF.als_step_A)
     WF.__dict__.setdefault("_orig_als_step_B", WF.als_step_B)
-    for mod in (W, W8, WR, WF, oracle):
+    import oracle.shared_svd as WS
+    WS.__dict__.setdefault("_orig_one", WS.decode_attn_shared_one)
+    for mod in (W, W8, WR, WF, WS, oracle):
         if hasattr(mod, attr):
             monkeypatch.setattr(mod, attr, fn)
     caught = []

@@ -604,3 +604,86 @@ def test_weighted_als_recovers_low_rank():
     F = rng.uniform(0.2, 5.0, (E, H))
     A, B = O.weighted_factors(W, F, rng.standard_normal((E, r)), rng.standard_normal((1, r, H)), 1, 60)
     assert O.weighted_objective(W, F, A, B, 1)[0] <= 1e-12 * np.sum(F * W * W)
+
+
+# ---------------------------------------------------------------------------
+# conventional (shared-latent) factorisation
+# ---------------------------------------------------------------------------
+def _shared_from_per_head(inp):
+    """Embed per-head latents and factors in one shared latent of rank
+    R = nh r: latent columns [h r, (h + 1) r) hold head h's latent, and the
+    factor is block diagonal (head h's rows only feed head h's columns)."""
+    from rank_kv_cache_flash_amd.inputs import SharedInputs
+    nb, nh, H, r, Lc = inp.nb, inp.nh, inp.H, inp.r, inp.L_cap
+    C_K = np.zeros((nb, Lc, nh * r), np.float32)
+    C_V = np.zeros_like(C_K)
+    B_K = np.zeros((nh * r, nh * H), np.float32)
+    B_V = np.zeros_like(B_K)
+    for h in range(nh):
+        C_K[:, :, h * r:(h + 1) * r] = inp.C_K[:, h]
+        C_V[:, :, h * r:(h + 1) * r] = inp.C_V[:, h]
+        B_K[h * r:(h + 1) * r, h * H:(h + 1) * H] = inp.B_K[h]
+        B_V[h * r:(h + 1) * r, h * H:(h + 1) * H] = inp.B_V[h]
+    return SharedInputs(nb=nb, nh=nh, H=H, R=nh * r, L_cap=Lc, q=np.asarray(inp.q, np.float32), C_K=C_K, C_V=C_V,
+                        B_K=B_K, B_V=B_V, L=inp.L, dt="f32")
+
+
+def test_shared_block_diagonal_equals_per_head():
+    from rank_kv_cache_flash_amd.inputs import make_decode_inputs
+    inp = make_decode_inputs(3, 4, 8, 3, np.array([7, 0, 1], np.int32), 8, seed=51, act_dt="f32", C_dt="f32",
+                             q_gain=6.0)
+    got = O.decode_attn_shared(_shared_from_per_head(inp))
+    assert np.allclose(got, O.decode_attn(inp), rtol=0, atol=1e-12)
+    assert not got[1].any()
+
+
+def test_shared_identity_factors_equal_library_attention():
+    """R = nh H and B = I: head h's keys are latent columns [h H, (h + 1) H)."""
+    from rank_kv_cache_flash_amd.inputs import SharedInputs
+    rng = np.random.default_rng(52)
+    nb, nh, H, ell = 2, 3, 4, 6
+    R = nh * H
+    q = rng.standard_normal((nb, nh, H)).astype(np.float32)
+    C_K = rng.standard_normal((nb, ell, R)).astype(np.float32)
+    C_V = rng.standard_normal((nb, ell, R)).astype(np.float32)
+    I = np.eye(R, dtype=np.float32)
+    inp = SharedInputs(nb=nb, nh=nh, H=H, R=R, L_cap=ell, q=q, C_K=C_K, C_V=C_V, B_K=I, B_V=I,
+                       L=np.array([ell, ell], np.int32), dt="f32")
+    got = O.decode_attn_shared(inp)
+    for b in range(nb):
+        for h in range(nh):
+            Q = torch.tensor(q[b, h], dtype=torch.float64).view(1, 1, 1, H)
+            K = torch.tensor(C_K[b, :, h * H:(h + 1) * H], dtype=torch.float64).view(1, 1, ell, H)
+            V = torch.tensor(C_V[b, :, h * H:(h + 1) * H], dtype=torch.float64).view(1, 1, ell, H)
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V).view(H).numpy()
+            assert np.allclose(got[b, h], ref, rtol=0, atol=1e-12)
+
+
+def test_shared_brute_force_loops():
+    from rank_kv_cache_flash_amd.inputs import SharedInputs
+    rng = np.random.default_rng(53)
+    nb, nh, H, R, ell = 2, 2, 3, 5, 4
+    q = rng.standard_normal((nb, nh, H)).astype(np.float32)
+    C_K = rng.standard_normal((nb, ell, R)).astype(np.float32)
+    C_V = rng.standard_normal((nb, ell, R)).astype(np.float32)
+    B_K = rng.standard_normal((R, nh * H)).astype(np.float32)
+    B_V = rng.standard_normal((R, nh * H)).astype(np.float32)
+    Ls = [4, 3]
+    inp = SharedInputs(nb=nb, nh=nh, H=H, R=R, L_cap=ell, q=q, C_K=C_K, C_V=C_V, B_K=B_K, B_V=B_V,
+                       L=np.array(Ls, np.int32), dt="f32")
+    got = O.decode_attn_shared(inp)
+    for b in range(nb):
+        for h in range(nh):
+            scores = []
+            for t in range(Ls[b]):
+                acc = 0.0
+                for j in range(H):
+                    k = sum(float(C_K[b, t, i]) * float(B_K[i, h * H + j]) for i in range(R))
+                    acc += float(q[b, h, j]) * k
+                scores.append(acc / math.sqrt(H))
+            m = max(scores)
+            w = [math.exp(s - m) for s in scores]
+            for j in range(H):
+                num = sum(w[t] * sum(float(C_V[b, t, i]) * float(B_V[i, h * H + j]) for i in range(R))
+                          for t in range(Ls[b]))
+                assert abs(got[b, h, j] - num / sum(w)) <= 1e-12
