@@ -386,6 +386,36 @@ int wsvd_weighted_update_B(int E, int nh, int H, int r, const float* W,
                            const float* F, const float* A, float* B,
                            hipStream_t stream);
 
+/*
+ * Ablation: decoding over a conventional (whole-matrix) factorisation, the
+ * scheme the per-head path replaces.  One latent of global rank R is shared
+ * by all heads and every head rebuilds its keys and values from it
+ * (Japanese page section 1, German page section 1, Italian page section 1,
+ * Arabic page section 1; per-head factors cut the latent to L x r and the
+ * rebuild cost by r / R, Arabic page section 2a).  Reading: head h's keys
+ * are C_K[b] B_K[:, hH:(h+1)H], values likewise.
+ *
+ *   q        BF16 [nb, nh, H]
+ *   C_K, C_V BF16 [nb, L_cap, R]   shared latent rows of each sequence
+ *   B_K, B_V BF16 [R, nh*H]        column block h maps the latent to head h
+ *   L        int32 [nb] (device), clamped to [0, L_cap]; 0 gives a zero row
+ *   out      F32 | BF16 [nb, nh, H]
+ * H in {64, 128}; R in {512, 1024, 2048}.  softmax_scale <= 0 means
+ * 1/sqrt(H); n_splits 0 = the same automatic rule as wsvd_decode_attn.
+ * Three launches: q' = B_K^T-block fold, split attention over the shared
+ * latent (every head streams the whole R-wide rows), merge + projection.
+ * Workspace: wsvd_shared_decode_workspace_bytes(...), 256-byte aligned, no
+ * initial contents required.
+ */
+size_t wsvd_shared_decode_workspace_bytes(int nb, int nh, int R, int L_cap, int n_splits);
+int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap,
+                            const int32_t* L, const void* q,
+                            const void* C_K, const void* C_V,
+                            const void* B_K, const void* B_V,
+                            float softmax_scale, int n_splits,
+                            void* workspace, size_t workspace_bytes,
+                            void* out, wsvd_dtype out_dt, hipStream_t stream);
+
 /* Static description of a status code.  Pure host; never NULL. */
 const char* wsvd_status_string(int status);
 

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwsvd.so")
 
-SOURCES = ["abi.hip", "decode.hip", "decode_rope.hip", "combine.hip", "append.hip", "w8a8.hip", "factorize.hip"]
+SOURCES = ["abi.hip", "decode.hip", "decode_rope.hip", "combine.hip", "append.hip", "w8a8.hip", "factorize.hip", "shared_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -412,5 +412,59 @@ int wsvd_weighted_update_B(int E, int nh, int H, int r, const float* W, const fl
                                                                                                 : WSVD_ERR_HIP;
 }
 
+static size_t shared_qp_bytes(int nb, int nh, int R) { return round_up((size_t)nb * nh * R * sizeof(float), 256); }
+static size_t shared_part_bytes(int nb, int nh, int R, int S) {
+    return round_up((size_t)nb * nh * S * R * sizeof(float), 256);
+}
+
+size_t wsvd_shared_decode_workspace_bytes(int nb, int nh, int R, int L_cap, int n_splits) {
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0 || R <= 0) return 0;
+    return shared_qp_bytes(nb, nh, R) + shared_part_bytes(nb, nh, R, S) +
+           round_up((size_t)nb * nh * S * sizeof(float), 256);
+}
+
+int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap, const int32_t* L, const void* q,
+                            const void* C_K, const void* C_V, const void* B_K, const void* B_V, float softmax_scale,
+                            int n_splits, void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt,
+                            hipStream_t stream) {
+    if (nb <= 0 || nh <= 0 || H <= 0 || R <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
+    if (nh > 4096 || (long long)nb * L_cap * R > (1ll << 40) || (long long)R * nh * H > (1ll << 40))
+        return WSVD_ERR_SHAPE;
+    if (!L || !q || !C_K || !C_V || !B_K || !B_V || !out) return WSVD_ERR_NULL;
+    if (out_dt != WSVD_F32 && out_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
+    if (!head_dim_ok(H) || (R != 512 && R != 1024 && R != 2048)) return WSVD_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(C_K) || !aligned16(C_V) || !aligned16(B_K) || !aligned16(B_V) ||
+        !aligned16(out) || !aligned16(L))
+        return WSVD_ERR_ALIGN;
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0) return WSVD_ERR_SHAPE;
+    if ((long long)nb * S * nh > (1ll << 31) - 4096) return WSVD_ERR_SHAPE;
+    const size_t need = wsvd_shared_decode_workspace_bytes(nb, nh, R, L_cap, n_splits);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+    wsvd::SharedArgs a;
+    a.nb = nb;
+    a.nh = nh;
+    a.H = H;
+    a.R = R;
+    a.L_cap = L_cap;
+    a.S = S;
+    a.L = L;
+    a.q = static_cast<const uint16_t*>(q);
+    a.C_K = static_cast<const uint16_t*>(C_K);
+    a.C_V = static_cast<const uint16_t*>(C_V);
+    a.B_K = static_cast<const uint16_t*>(B_K);
+    a.B_V = static_cast<const uint16_t*>(B_V);
+    const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
+    a.scale_log2 = sigma * wsvd::kLog2e;
+    char* ws = static_cast<char*>(workspace);
+    a.qp = reinterpret_cast<float*>(ws);
+    a.o_part = reinterpret_cast<float*>(ws + shared_qp_bytes(nb, nh, R));
+    a.lse_part = reinterpret_cast<float*>(ws + shared_qp_bytes(nb, nh, R) + shared_part_bytes(nb, nh, R, S));
+    a.out = out;
+    a.out_dt = (int)out_dt;
+    return wsvd::launch_shared_decode(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
 }  // extern "C"
 

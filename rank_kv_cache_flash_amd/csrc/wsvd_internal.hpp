@@ -91,4 +91,24 @@ hipError_t launch_factorize_svd(const float* W, int E, int nh, int H, int r, flo
 hipError_t launch_factorize_weighted(bool rows, const float* W, const float* F, const float* in, int E, int nh,
                                      int H, int r, float* out, hipStream_t st);
 
+// Decode over a conventional shared rank-R latent (shared_decode.hip):
+// bf16 q [nb, nh, H], C_K / C_V [nb, L_cap, R], B_K / B_V [R, nh*H].
+struct SharedArgs {
+    int nb, nh, H, R, L_cap, S;
+    const int32_t* L;
+    const uint16_t* q;
+    const uint16_t* C_K;
+    const uint16_t* C_V;
+    const uint16_t* B_K;
+    const uint16_t* B_V;
+    float scale_log2;
+    float* qp;        // fp32 [nb, nh, R]
+    float* o_part;    // fp32 [nb, nh, S, R]
+    float* lse_part;  // fp32 [nb, nh, S]
+    void* out;        // [nb, nh, H]
+    int out_dt;
+};
+
+hipError_t launch_shared_decode(const SharedArgs& a, hipStream_t st);
+
 }  // namespace wsvd

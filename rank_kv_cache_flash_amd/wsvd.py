@@ -76,6 +76,11 @@ def lib() -> ctypes.CDLL:
     L.wsvd_weighted_update_A.restype = i32
     L.wsvd_weighted_update_B.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.wsvd_weighted_update_B.restype = i32
+    L.wsvd_shared_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.wsvd_shared_decode_workspace_bytes.restype = sz
+    L.wsvd_shared_decode_attn.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, i32, vp, sz, vp, i32,
+                                          vp]
+    L.wsvd_shared_decode_attn.restype = i32
     L.wsvd_status_string.argtypes = [i32]
     L.wsvd_status_string.restype = ctypes.c_char_p
     L.wsvd_version.argtypes = []
@@ -417,6 +422,40 @@ def weighted_update_B(W, F, A, nh, *, out=None, stream=None):
     _check(lib().wsvd_weighted_update_B(E, nh, H, r, _ptr(W), _ptr(F), _ptr(A), _ptr(B), _stream(stream)),
            "wsvd_weighted_update_B")
     return B
+
+
+def shared_decode_workspace_bytes(nb, nh, R, L_cap, n_splits=0) -> int:
+    return int(lib().wsvd_shared_decode_workspace_bytes(nb, nh, R, L_cap, n_splits))
+
+
+def shared_decode_attn(q, C_K, C_V, B_K, B_V, L, *, softmax_scale=None, n_splits=None, out=None, out_dtype=None,
+                       workspace=None, stream=None):
+    """wsvd_shared_decode_attn: q [nb, nh, H]; C_K / C_V [nb, L_cap, R] and
+    B_K / B_V [R, nh*H], all bfloat16; L int32 [nb]."""
+    for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"), (out, "out"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    nb, nh, H = q.shape
+    L_cap, R = C_K.shape[1], C_K.shape[2]
+    if workspace is None:
+        workspace = torch.empty(max(shared_decode_workspace_bytes(nb, nh, R, L_cap, n_splits or 0), 256),
+                                dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((nb, nh, H), dtype=out_dtype or q.dtype, device=q.device)
+    st = lib().wsvd_shared_decode_attn(nb, nh, H, R, L_cap, _ptr(L), _ptr(q), _ptr(C_K), _ptr(C_V), _ptr(B_K),
+                                       _ptr(B_V), float(softmax_scale or 0.0), int(n_splits or 0), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(out), _DT[out.dtype],
+                                       _stream(stream))
+    _check(st, "wsvd_shared_decode_attn")
+    return out
+
+
+def shared_device_inputs(inp, device="cuda"):
+    """SharedInputs (numpy, bf16 bit patterns) -> dict of GPU tensors."""
+    return {"q": to_device(inp.q, inp.dt, device), "C_K": to_device(inp.C_K, inp.dt, device),
+            "C_V": to_device(inp.C_V, inp.dt, device), "B_K": to_device(inp.B_K, inp.dt, device),
+            "B_V": to_device(inp.B_V, inp.dt, device),
+            "L": to_device(inp.L, "i32", device)}
 
 
 def to_device(arr, dt: str, device="cuda"):

@@ -280,3 +280,30 @@ def test_weighted_update_rejects(L, fn, args, want):
     v = ctypes.c_void_p
     conv = [a if i < 4 else (v(a) if a else None) for i, a in enumerate(args)]
     assert getattr(L, fn)(*conv, None) == want
+
+
+def shared(L, nb=2, nh=4, H=128, R=1024, Lc=256, Lp=P, q=P, CK=P, CV=P, BK=P, BV=P, S=0, ws=P, wsb=16, out=P,
+           out_dt=BF16):
+    v = ctypes.c_void_p
+    pp = lambda x: v(x) if x else None
+    return L.wsvd_shared_decode_attn(nb, nh, H, R, Lc, pp(Lp), pp(q), pp(CK), pp(CV), pp(BK), pp(BV), 0.0, S, pp(ws),
+                                     wsb, pp(out), out_dt, None)
+
+
+def test_shared_workspace_size(L):
+    f = wsvd.shared_decode_workspace_bytes
+    for nb, nh, R, Lc, S in [(1, 32, 1024, 1088, 0), (16, 32, 2048, 4096, 3), (3, 5, 512, 100, 7)]:
+        s = wsvd.decode_num_splits(nb, nh, Lc, S)
+        assert f(nb, nh, R, Lc, S) >= nb * nh * R * 4 + nb * nh * s * (R + 1) * 4
+    assert f(0, 32, 1024, 100, 0) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), ESHAPE), (dict(R=0), ESHAPE), (dict(S=-1), ESHAPE), (dict(S=300, Lc=256), ESHAPE),
+    (dict(Lp=None), ENULL), (dict(CV=None), ENULL), (dict(BV=None), ENULL), (dict(out=None), ENULL),
+    (dict(out_dt=I8), EDTYPE), (dict(out_dt=F16), EDTYPE), (dict(H=96), EUNSUP), (dict(R=768), EUNSUP),
+    (dict(R=256), EUNSUP), (dict(q=P + 2), EALIGN), (dict(BK=P + 8), EALIGN), ({}, EWS), (dict(ws=None), EWS),
+    (dict(ws=P + 16, wsb=1 << 40), EWS),
+])
+def test_shared_rejects(L, kw, want):
+    assert shared(L, **kw) == want
