@@ -352,6 +352,81 @@ def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
 
 
 # ---------------------------------------------------------------------------
+# ablation: conventional shared-latent decode at the same cache size
+# ---------------------------------------------------------------------------
+SHARED_SHAPES = {2: (1, 32, 128, 32, 1088), 3: (16, 32, 128, 64, 4096)}
+
+
+def _shared_calls(nb, nh, H, R, L_cap, Lt, g, copies, out):
+    import torch
+    from rank_kv_cache_flash_amd import wsvd
+    bf = torch.bfloat16
+    ws = torch.empty(wsvd.shared_decode_workspace_bytes(nb, nh, R, L_cap, 0), dtype=torch.uint8, device="cuda")
+    calls = []
+    for _ in range(copies):
+        q = (torch.randn(nb, nh, H, generator=g, device="cuda") * H ** -0.5).to(bf)
+        CK = (torch.randn(nb, L_cap, R, generator=g, device="cuda") * R ** -0.5).to(bf)
+        CV = (torch.randn(nb, L_cap, R, generator=g, device="cuda") * R ** -0.5).to(bf)
+        BK = (torch.randn(R, nh * H, generator=g, device="cuda") * H ** -0.5).to(bf)
+        BV = (torch.randn(R, nh * H, generator=g, device="cuda") * H ** -0.5).to(bf)
+        calls.append(lambda q=q, CK=CK, CV=CV, BK=BK, BV=BV: wsvd.shared_decode_attn(q, CK, CV, BK, BV, Lt,
+                                                                                     workspace=ws, out=out))
+    return calls
+
+
+def shared_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
+    """Per-head decode (rank r per head) against the conventional shared
+    latent of the same cache size (R = nh r), on equal shapes: random GPU
+    bf16 inputs (parity is covered by the tests), cold-HBM rotation for
+    both, graph replay.  Reports both step times, the bytes each must read
+    and the rebuild-cost ratio."""
+    import numpy as np
+    import torch
+    from rank_kv_cache_flash_amd import wsvd
+
+    R = nh * r
+    L_cap = int(L)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    bf = torch.bfloat16
+    Lt = torch.full((nb,), L_cap, dtype=torch.int32, device="cuda")
+    out = torch.empty(nb, nh, H, dtype=bf, device="cuda")
+    latent = nb * L_cap * 2 * R * 2                       # the same for both schemes
+    w_fact = nh * 2 * r * H * 2
+    s_fact = 2 * R * nh * H * 2                           # B_K once, B_V once per 8 sequences (lower bound)
+    wb = latent + w_fact + 2 * nb * nh * H * 2
+    sb_unique = latent + s_fact + 2 * nb * nh * H * 2
+    sb_streamed = nh * latent + s_fact + 2 * nb * nh * H * 2
+
+    def copies_for(nbytes):
+        return max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
+
+    ws = wsvd.decode_workspace(nb, nh, H, L_cap, 0)
+    w_calls = []
+    for _ in range(copies_for(wb)):
+        q = (torch.randn(nb, nh, H, generator=g, device="cuda") * H ** -0.5).to(bf)
+        CK = (torch.randn(nb, nh, L_cap, r, generator=g, device="cuda") * r ** -0.5).to(bf)
+        CV = (torch.randn(nb, nh, L_cap, r, generator=g, device="cuda") * r ** -0.5).to(bf)
+        BK = (torch.randn(nh, r, H, generator=g, device="cuda") * H ** -0.5).to(bf)
+        BV = (torch.randn(nh, r, H, generator=g, device="cuda") * H ** -0.5).to(bf)
+        w_calls.append(wsvd.PreparedDecode(q, CK, CV, BK, BV, Lt, workspace=ws, out=out))
+    t_w = graph_time(lambda i: w_calls[i % len(w_calls)](), steps, warmup)[0]
+    del w_calls
+    torch.cuda.empty_cache()
+    s_calls = _shared_calls(nb, nh, H, R, L_cap, Lt, g, copies_for(sb_unique), out)
+    t_s = graph_time(lambda i: s_calls[i % len(s_calls)](), steps, warmup)[0]
+    del s_calls
+    torch.cuda.empty_cache()
+    return {"nb": nb, "nh": nh, "H": H, "r": r, "R": R, "L": L_cap, "r_over_R": round(r / R, 5),
+            "latent_bytes_each": latent, "factor_bytes_per_head": w_fact, "factor_bytes_shared": s_fact,
+            "per_head_us": round(t_w * 1e6, 3), "shared_us": round(t_s * 1e6, 3),
+            "shared_over_per_head": round(t_s / t_w, 2),
+            "rebuild_macs_per_token_head": {"per_head": 2 * r, "shared": 2 * R},
+            "shared_bytes_if_every_head_streams_from_hbm": sb_streamed,
+            "shared_effective_GB_per_s_unique": round(sb_unique / t_s / 1e9, 1),
+            "per_head_GB_per_s": round(wb / t_w / 1e9, 1)}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host (bounded sample)
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, gpu_out, budget_s=12.0):
@@ -452,11 +527,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep",
-                                       "factorize-loop"],
+                                       "factorize-loop", "shared-loop"],
                     default="bench",
                     help="decode-loop / step-loop / copy-calib / counters: plain launch loops for traces and counters")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--no-shared", dest="shared", action="store_false",
+                    help="skip the shared-latent (conventional factorisation) ablation")
     ap.add_argument("--no-factorize", dest="factorize", action="store_false",
                     help="skip timing the offline per-head factorisation")
     args = ap.parse_args()
@@ -522,6 +599,22 @@ def main():
             del w
             torch.cuda.empty_cache()
         print(json.dumps(rec))
+        return
+    if args.mode == "shared-loop":
+        # Plain launch loop of the shared-latent decode at the cache size of
+        # workload --config (2 or 3), for kernel traces and counters.
+        nb_, nh_, H_, r_, L_ = SHARED_SHAPES[args.config]
+        R_ = nh_ * r_
+        g = torch.Generator(device="cuda").manual_seed(0)
+        Lt = torch.full((nb_,), L_, dtype=torch.int32, device="cuda")
+        out = torch.empty(nb_, nh_, H_, dtype=torch.bfloat16, device="cuda")
+        lat = nb_ * L_ * 2 * R_ * 2
+        calls = _shared_calls(nb_, nh_, H_, R_, L_, Lt, g, max(1, min(64, math.ceil(COLD_BYTES / lat))), out)
+        for i in range(args.steps):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": args.mode, "shape": f"nb={nb_} nh={nh_} H={H_} R={R_} L={L_}",
+                          "launches": args.steps, "latent_bytes": lat}))
         return
     if args.mode == "factorize-loop":
         # Plain launch loop for kernel traces: per-head SVD at rank 32, then
@@ -595,6 +688,14 @@ def main():
         if c.has_append:
             per[c.name]["append_alone"] = append_variants(c, max(k, 100), min(args.warmup, 10))
 
+    ablation = None
+    if args.shared:
+        ablation = {}
+        for cid, (nb_, nh_, H_, r_, L_) in SHARED_SHAPES.items():
+            k = 200 if cid == 2 else 10
+            ablation[CONFIGS[cid].name] = shared_vs_wsvd(nb_, nh_, H_, r_, L_, k, min(args.warmup, 5))
+            torch.cuda.empty_cache()
+
     offline = None
     if args.factorize:
         offline = factorize_offline(cpu=not args.no_cpu)
@@ -623,6 +724,7 @@ def main():
         "vs_dense_flash_decoding": vs_dense,
         "rotary_keys": rope_main,
         "per_config": per,
+        "shared_latent_ablation": ablation,
         "offline_factorize": offline,
         "kernel_src": kernel_src_hash(),
     }

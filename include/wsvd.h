@@ -402,8 +402,9 @@ int wsvd_weighted_update_B(int E, int nh, int H, int r, const float* W,
  *   out      F32 | BF16 [nb, nh, H]
  * H in {64, 128}; R in {512, 1024, 2048}.  softmax_scale <= 0 means
  * 1/sqrt(H); n_splits 0 = the same automatic rule as wsvd_decode_attn.
- * Three launches: q' = B_K^T-block fold, split attention over the shared
- * latent (every head streams the whole R-wide rows), merge + projection.
+ * Four launches: the q' = B_K-block fold, split attention over the shared
+ * latent (every head streams the whole R-wide rows), merge + projection in
+ * chunks of 128 latent columns, and the sum of the chunks.
  * Workspace: wsvd_shared_decode_workspace_bytes(...), 256-byte aligned, no
  * initial contents required.
  */

@@ -417,11 +417,16 @@ static size_t shared_part_bytes(int nb, int nh, int R, int S) {
     return round_up((size_t)nb * nh * S * R * sizeof(float), 256);
 }
 
+// fp32 [R / 128, nb, nh, H] chunk contributions of the projection (H <= 128).
+static size_t shared_proj_bytes(int nb, int nh, int R) {
+    return round_up((size_t)((R + 127) / 128) * nb * nh * 128 * sizeof(float), 256);
+}
+
 size_t wsvd_shared_decode_workspace_bytes(int nb, int nh, int R, int L_cap, int n_splits) {
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0 || R <= 0) return 0;
     return shared_qp_bytes(nb, nh, R) + shared_part_bytes(nb, nh, R, S) +
-           round_up((size_t)nb * nh * S * sizeof(float), 256);
+           round_up((size_t)nb * nh * S * sizeof(float), 256) + shared_proj_bytes(nb, nh, R);
 }
 
 int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap, const int32_t* L, const void* q,
@@ -461,6 +466,8 @@ int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap, const int32
     a.qp = reinterpret_cast<float*>(ws);
     a.o_part = reinterpret_cast<float*>(ws + shared_qp_bytes(nb, nh, R));
     a.lse_part = reinterpret_cast<float*>(ws + shared_qp_bytes(nb, nh, R) + shared_part_bytes(nb, nh, R, S));
+    a.proj_part = reinterpret_cast<float*>(ws + shared_qp_bytes(nb, nh, R) + shared_part_bytes(nb, nh, R, S) +
+                                           round_up((size_t)nb * nh * S * sizeof(float), 256));
     a.out = out;
     a.out_dt = (int)out_dt;
     return wsvd::launch_shared_decode(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;

@@ -13,14 +13,16 @@
 // The same fold as the per-head kernel applies -- s_t = C_K[b, t] . q'_h
 // with q'_h = B_K[:, hH:(h+1)H] q_h -- so nothing of size L x H is ever
 // formed; what remains is the defining cost of the scheme: every head
-// streams the whole R-wide shared latent.  Three launches:
+// streams the whole R-wide shared latent.  Four launches:
 //   shared_fold_kernel   q'[b, h, :] (fp32), B_K read once per step;
 //   shared_split_kernel  one block per (b, h, split): the shared latent
 //                        rows of the split, one row per wave-wide pass
 //                        (R / 64 elements per lane), online softmax, and the
 //                        R-wide value accumulation; partials are R wide;
-//   shared_merge_kernel  per (h, group of sequences): merge the partials
-//                        and project through B_V[:, hH:(h+1)H].
+//   shared_merge_kernel  per (h, chunk of 128 latent columns, group of 8
+//                        sequences): merge the partials on those columns and
+//                        multiply by the same rows of B_V[:, hH:(h+1)H];
+//   shared_sum_kernel    adds the chunk contributions in order.
 // The latent is read with ordinary (cached) loads: the nh blocks of one
 // sequence and split read the same rows, and they are placed on one XCD so
 // that the repeats can be served from its L2.
@@ -30,8 +32,9 @@
 namespace wsvd {
 namespace {
 
-constexpr int kFoldRows = 8;      // rows of B_K per fold block
+constexpr int kFoldRows = 4;      // rows of B_K per fold block
 constexpr int kMergeSeqs = 8;     // sequences per merge block
+constexpr int kMergeRows = 128;   // latent columns per merge block
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -41,35 +44,42 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, size_t i) { return _
 __device__ __forceinline__ float wave_sum(float v) { return xor32_sum(xor16_sum(group_sum<16>(v))); }
 
 // ---------------------------------------------------------------------------
-// q'[b, h, k] = scale_log2 * sum_j B_K[k, hH + j] q[b, h, j].  Block (x, h):
-// rows k in [8x, 8x + 8); 32 lanes per row, H / 32 elements per lane.
+// q'[b, h, k] = scale_log2 * sum_j B_K[k, hH + j] q[b, h, j].  Block (x, y):
+// rows [kFoldRows x, +kFoldRows) and columns [2048 y, 2048 y + 2048) of B_K;
+// each thread holds 8 consecutive columns (one 16-byte load per row), so the
+// H / 8 threads of a head reduce over DPP.  A thread's slice of q[b, h] is
+// loaded once per sequence and used for all of the block's rows.
 template <int H>
 __global__ __launch_bounds__(256) void shared_fold_kernel(int nb, int nh, int R, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ B_K, float scale_log2,
                                                           float* __restrict__ qp) {
-    constexpr int EP = H / 32;
-    const int tid = threadIdx.x, row = tid >> 5, part = tid & 31;
-    const int h = blockIdx.y;
-    const int k = blockIdx.x * kFoldRows + row;
-    const bool live = k < R;
+    constexpr int GL = H / 8;  // lanes per head
+    const int tid = threadIdx.x;
     const size_t ld = (size_t)nh * H;
-    float bk[EP];
+    const size_t col = (size_t)blockIdx.y * 2048 + (size_t)tid * 8;
+    const bool live_c = col < ld;
+    const int h = (int)(col / H);
+    const int e0 = (int)(col % H);
+    const int k0 = blockIdx.x * kFoldRows;
+    u32x4 bk[kFoldRows];
 #pragma unroll
-    for (int e = 0; e < EP; ++e) bk[e] = live ? bf16_at(B_K, (size_t)k * ld + (size_t)h * H + part * EP + e) : 0.f;
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-        float qv[8][EP];
+    for (int i = 0; i < kFoldRows; ++i) {
+        bk[i] = u32x4{0u, 0u, 0u, 0u};
+        if (live_c && k0 + i < R) bk[i] = *reinterpret_cast<const u32x4*>(B_K + (size_t)(k0 + i) * ld + col);
+    }
+    for (int b = 0; b < nb; ++b) {
+        u32x4 qw = u32x4{0u, 0u, 0u, 0u};
+        if (live_c) qw = *reinterpret_cast<const u32x4*>(q + ((size_t)b * nh + h) * H + e0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int e = 0; e < EP; ++e)
-                qv[u][e] = (b0 + u < nb) ? bf16_at(q, ((size_t)(b0 + u) * nh + h) * H + part * EP + e) : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int i = 0; i < kFoldRows; ++i) {
             float p = 0.f;
 #pragma unroll
-            for (int e = 0; e < EP; ++e) p = fmaf(bk[e], qv[u][e], p);
-            p = xor16_sum(group_sum<16>(p));  // the 32 lanes of this row
-            if (live && part == 0 && b0 + u < nb) qp[((size_t)(b0 + u) * nh + h) * R + k] = p * scale_log2;
+            for (int w = 0; w < 4; ++w) {
+                p = fmaf(bf16_lo(bk[i][w]), bf16_lo(qw[w]), p);
+                p = fmaf(bf16_hi(bk[i][w]), bf16_hi(qw[w]), p);
+            }
+            p = group_sum<GL>(p);
+            if (live_c && (tid % GL) == 0 && k0 + i < R) qp[((size_t)b * nh + h) * R + k0 + i] = p * scale_log2;
         }
     }
 }
@@ -231,90 +241,125 @@ __global__ __launch_bounds__(256) void shared_split_kernel(int nb, int nh, int S
 }
 
 // ---------------------------------------------------------------------------
-// Merge + projection.  Block (h, y): sequences [8y, 8y + 8); the merged
-// R-wide vectors go to LDS, then thread (j, part) sums its share of the R
-// rows of B_V[:, hH + j] for every sequence of the group.
-template <int H, int R>
-__global__ __launch_bounds__(256) void shared_merge_kernel(int nb, int nh, int S, const float* __restrict__ o_part,
+// Merge + projection, split over chunks of kMergeRows latent columns.  Block
+// (h, c, y): for sequences [8y, 8y + 8) it merges the split partials on
+// columns [128c, 128c + 128) only, then multiplies them by the same rows of
+// B_V[:, hH:(h+1)H] (thread (kl, cg): 8 output columns cg, rows kl, kl + NKL,
+// ..., 16-byte loads) and stores the chunk's contribution; shared_sum_kernel
+// adds the chunks in order.
+template <int H>
+__global__ __launch_bounds__(256) void shared_merge_kernel(int nb, int nh, int S, int R,
+                                                           const float* __restrict__ o_part,
                                                            const float* __restrict__ lse_part,
-                                                           const uint16_t* __restrict__ B_V, void* out,
-                                                           int out_dt) {
-    constexpr int NPART = 256 / H;
-    constexpr int KP = R / NPART;
-    __shared__ float sh_o[kMergeSeqs][R];
-    __shared__ float sh_w[kMergeSeqs][64];
-    __shared__ float sh_red[NPART][kMergeSeqs][H];
+                                                           const uint16_t* __restrict__ B_V,
+                                                           float* __restrict__ proj_part) {
+    constexpr int GL = H / 8;        // threads per B_V row slice
+    constexpr int NKL = 256 / GL;    // rows in flight
+    __shared__ float sh_o[kMergeSeqs][kMergeRows];
+    __shared__ float sh_w[64];
+    __shared__ float sh_red[4][kMergeSeqs][H];
     const int tid = threadIdx.x;
-    const int h = blockIdx.x;
-    const int b0 = blockIdx.y * kMergeSeqs;
+    const int h = blockIdx.x, c = blockIdx.y;
+    const int b0 = blockIdx.z * kMergeSeqs;
     const int nbg = min(kMergeSeqs, nb - b0);
+    const int k0 = c * kMergeRows;
 
-    for (int u = 0; u < nbg; ++u) {
-        const size_t bh = (size_t)(b0 + u) * nh + h;
-        const float* lsp = lse_part + bh * S;
-        float Mx = kNegInf;
-        for (int s = 0; s < S; ++s) Mx = fmaxf(Mx, lsp[s]);
-        // Weights in chunks of 64 splits through LDS; partial vectors summed
-        // in split order.
-        float accs[R / 256];
-#pragma unroll
-        for (int i = 0; i < R / 256; ++i) accs[i] = 0.f;
-        float wsum = 0.f;
-        for (int s0 = 0; s0 < S; s0 += 64) {
-            const int n = min(64, S - s0);
-            __syncthreads();
-            if (tid < n) {
-                const float lv = lsp[s0 + tid];
-                sh_w[u][tid] = (lv == kNegInf) ? 0.f : fast_exp2((lv - Mx) * kLog2e);
-            }
-            __syncthreads();
-            for (int s = 0; s < n; ++s) {
-                const float w = sh_w[u][s];
-                wsum += w;
-                const float* op = o_part + (bh * S + s0 + s) * R;
-#pragma unroll
-                for (int i = 0; i < R / 256; ++i) accs[i] = fmaf(w, op[tid + 256 * i], accs[i]);
+    for (int u = 0; u < kMergeSeqs; ++u) {
+        float acc = 0.f, wsum = 0.f;
+        if (u < nbg) {
+            const size_t bh = (size_t)(b0 + u) * nh + h;
+            const float* lsp = lse_part + bh * S;
+            float Mx = kNegInf;
+            for (int s = 0; s < S; ++s) Mx = fmaxf(Mx, lsp[s]);
+            for (int s0 = 0; s0 < S; s0 += 64) {
+                const int n = min(64, S - s0);
+                __syncthreads();
+                if (tid < n) {
+                    const float lv = lsp[s0 + tid];
+                    sh_w[tid] = (lv == kNegInf) ? 0.f : fast_exp2((lv - Mx) * kLog2e);
+                }
+                __syncthreads();
+                if (tid < kMergeRows) {
+                    for (int s = 0; s < n; ++s) {
+                        const float w = sh_w[s];
+                        wsum += w;
+                        acc = fmaf(w, o_part[(bh * S + s0 + s) * R + k0 + tid], acc);
+                    }
+                }
             }
         }
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-        for (int i = 0; i < R / 256; ++i) sh_o[u][tid + 256 * i] = accs[i] * inv;
+        if (tid < kMergeRows) sh_o[u][tid] = wsum > 0.f ? acc / wsum : 0.f;
     }
     __syncthreads();
 
-    const int j = tid % H, part = tid / H;
+    const int cg = tid % GL, kl = tid / GL;
     const size_t ld = (size_t)nh * H;
-    float o[kMergeSeqs];
+    float o[kMergeSeqs][8];
 #pragma unroll
-    for (int u = 0; u < kMergeSeqs; ++u) o[u] = 0.f;
-    for (int k = part * KP; k < (part + 1) * KP; ++k) {
-        const float bv = bf16_at(B_V, (size_t)k * ld + (size_t)h * H + j);
+    for (int u = 0; u < kMergeSeqs; ++u)
 #pragma unroll
-        for (int u = 0; u < kMergeSeqs; ++u) o[u] = fmaf(sh_o[u][k], bv, o[u]);
+        for (int e = 0; e < 8; ++e) o[u][e] = 0.f;
+    for (int k = kl; k < kMergeRows; k += NKL) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(B_V + (size_t)(k0 + k) * ld + (size_t)h * H + cg * 8);
+#pragma unroll
+        for (int u = 0; u < kMergeSeqs; ++u) {
+            const float ov = sh_o[u][k];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                o[u][2 * w] = fmaf(ov, bf16_lo(bv[w]), o[u][2 * w]);
+                o[u][2 * w + 1] = fmaf(ov, bf16_hi(bv[w]), o[u][2 * w + 1]);
+            }
+        }
     }
+    // Rows kl of one wave: lanes that differ in the bits above log2(GL).
+    const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int u = 0; u < kMergeSeqs; ++u) sh_red[part][u][j] = o[u];
+    for (int u = 0; u < kMergeSeqs; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = o[u][e];
+            for (int m = GL; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+            o[u][e] = v;
+        }
+    if (lane < GL) {
+#pragma unroll
+        for (int u = 0; u < kMergeSeqs; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sh_red[wave][u][cg * 8 + e] = o[u][e];
+    }
     __syncthreads();
     for (int i = tid; i < nbg * H; i += 256) {
-        const int u = i / H, jj = i % H;
-        float v = 0.f;
-#pragma unroll
-        for (int p = 0; p < NPART; ++p) v += sh_red[p][u][jj];
-        store_elem_wt(out, out_dt, ((size_t)(b0 + u) * nh + h) * H + jj, v);
+        const int u = i / H, j = i % H;
+        const float v = sh_red[0][u][j] + sh_red[1][u][j] + sh_red[2][u][j] + sh_red[3][u][j];
+        proj_part[(((size_t)c * nb + b0 + u) * nh + h) * H + j] = v;
     }
+}
+
+// out[b, h, :] = sum over the R / kMergeRows chunk contributions, in order.
+__global__ __launch_bounds__(256) void shared_sum_kernel(long n, int nc, const float* __restrict__ proj_part,
+                                                         void* out, int out_dt) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = 0.f;
+    for (int c = 0; c < nc; ++c) v += proj_part[(size_t)c * n + i];
+    store_elem_wt(out, out_dt, (size_t)i, v);
 }
 
 template <int H, int R>
 hipError_t launch_shared_hr(const SharedArgs& a, hipStream_t st) {
     constexpr int U = R >= 2048 ? 2 : 4;
-    hipLaunchKernelGGL((shared_fold_kernel<H>), dim3((a.R + kFoldRows - 1) / kFoldRows, a.nh), dim3(256), 0, st, a.nb,
-                       a.nh, a.R, a.q, a.B_K, a.scale_log2, a.qp);
+    const long cols = (long)a.nh * H;
+    hipLaunchKernelGGL((shared_fold_kernel<H>), dim3(R / kFoldRows, (unsigned)((cols + 2047) / 2048)), dim3(256), 0,
+                       st, a.nb, a.nh, R, a.q, a.B_K, a.scale_log2, a.qp);
     const long streams = (long)a.nb * a.S;
     const long padded = (streams + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL((shared_split_kernel<R, U>), dim3((unsigned)(padded * a.nh)), dim3(256), 0, st, a.nb, a.nh,
                        a.S, a.L_cap, a.L, a.C_K, a.C_V, a.qp, a.o_part, a.lse_part);
-    hipLaunchKernelGGL((shared_merge_kernel<H, R>), dim3(a.nh, (a.nb + kMergeSeqs - 1) / kMergeSeqs), dim3(256), 0,
-                       st, a.nb, a.nh, a.S, a.o_part, a.lse_part, a.B_V, a.out, a.out_dt);
+    hipLaunchKernelGGL((shared_merge_kernel<H>), dim3(a.nh, R / kMergeRows, (a.nb + kMergeSeqs - 1) / kMergeSeqs),
+                       dim3(256), 0, st, a.nb, a.nh, a.S, R, a.o_part, a.lse_part, a.B_V, a.proj_part);
+    const long n = (long)a.nb * a.nh * H;
+    hipLaunchKernelGGL(shared_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, R / kMergeRows,
+                       a.proj_part, a.out, a.out_dt);
     return hipGetLastError();
 }
 

@@ -105,6 +105,7 @@ struct SharedArgs {
     float* qp;        // fp32 [nb, nh, R]
     float* o_part;    // fp32 [nb, nh, S, R]
     float* lse_part;  // fp32 [nb, nh, S]
+    float* proj_part; // fp32 [R / 128, nb, nh, H]
     void* out;        // [nb, nh, H]
     int out_dt;
 };
