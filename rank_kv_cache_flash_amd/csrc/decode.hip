@@ -81,6 +81,21 @@ __device__ __forceinline__ float raw_elem(const void* base, int idx) {
     }
 }
 
+// int8 codes as exact fp16 values: byte c + 128 placed in the mantissa of
+// 1024 (fp16 0x6400 | u = 1024 + u), two codes per dword by one byte
+// permute, so each code then costs one mixed-precision FMA (fp16 operand,
+// fp32 accumulate) instead of a conversion and an FMA.  Every value carries
+// an offset of kI8Offset = 1024 + 128, removed once per row (scores) and once
+// per split (values).
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+constexpr float kI8Offset = 1152.f;
+__device__ __forceinline__ h2 i8_pair_lo(uint32_t w) {
+    return __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, 0x04010400u));
+}
+__device__ __forceinline__ h2 i8_pair_hi(uint32_t w) {
+    return __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, 0x04030402u));
+}
+
 // Dot of one 16-byte latent chunk with the lane's slice of q'.
 template <int CT>
 __device__ __forceinline__ float chunk_dot(const u32x4& d, const float* qp) {
@@ -97,15 +112,17 @@ __device__ __forceinline__ float chunk_dot(const u32x4& d, const float* qp) {
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t u = d[k] ^ 0x80808080u;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc = fmaf(qp[4 * k + c], float((u >> (8 * c)) & 0xffu), acc);
+            const h2 lo = i8_pair_lo(d[k]), hi = i8_pair_hi(d[k]);
+            acc = fmaf(qp[4 * k + 0], (float)lo.x, acc);
+            acc = fmaf(qp[4 * k + 1], (float)lo.y, acc);
+            acc = fmaf(qp[4 * k + 2], (float)hi.x, acc);
+            acc = fmaf(qp[4 * k + 3], (float)hi.y, acc);
         }
     }
     return acc;
 }
 
-// acc += w * chunk (int8: w * (byte + 128); the offset is removed later).
+// acc += w * chunk (int8: w * (code + kI8Offset); the offset is removed later).
 template <int CT>
 __device__ __forceinline__ void chunk_axpy(const u32x4& d, float w, float* acc) {
     if constexpr (CT == WSVD_F32) {
@@ -120,9 +137,11 @@ __device__ __forceinline__ void chunk_axpy(const u32x4& d, float w, float* acc) 
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t u = d[k] ^ 0x80808080u;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[4 * k + c] = fmaf(w, float((u >> (8 * c)) & 0xffu), acc[4 * k + c]);
+            const h2 lo = i8_pair_lo(d[k]), hi = i8_pair_hi(d[k]);
+            acc[4 * k + 0] = fmaf(w, (float)lo.x, acc[4 * k + 0]);
+            acc[4 * k + 1] = fmaf(w, (float)lo.y, acc[4 * k + 1]);
+            acc[4 * k + 2] = fmaf(w, (float)hi.x, acc[4 * k + 2]);
+            acc[4 * k + 3] = fmaf(w, (float)hi.y, acc[4 * k + 3]);
         }
     }
 }
@@ -291,11 +310,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         float qp[EPC];
 #pragma unroll
         for (int c = 0; c < EPC; ++c) qp[c] = act ? sh_qp[min(j, G - 1) * EPC + c] : 0.f;
-        float qoff = 0.f;  // int8: 128 * sum of the lane's q' slice
+        float qoff = 0.f;  // int8: kI8Offset * sum of the lane's q' slice
         if constexpr (I8) {
 #pragma unroll
             for (int c = 0; c < EPC; ++c) qoff += qp[c];
-            qoff *= 128.f;
+            qoff *= kI8Offset;
         }
 
         // ---- hot loop ----------------------------------------------------------
@@ -316,13 +335,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 sc[u] = (tbc + u * RW + g) < ntok ? d : kNegInf;
                 mloc = fmaxf(mloc, sc[u]);
             }
-            const float mn = fmaxf(m, mloc);
-            const float mu = (mn == kNegInf) ? 0.f : mn;
-            const float alpha = fast_exp2(m - mu);
-            l *= alpha;
-            if constexpr (I8) pw *= alpha;
+            // The reference max moves only when some lane's new scores pass it
+            // by 2^8 (log2 units): the weights exp2(s - m) then stay below 256
+            // and the accumulators are not rescaled on every tile.
+            if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f) != 0) {
+                const float mn = fmaxf(m, mloc);
+                const float alpha = fast_exp2(m - ((mn == kNegInf) ? 0.f : mn));
+                l *= alpha;
+                if constexpr (I8) pw *= alpha;
 #pragma unroll
-            for (int c = 0; c < EPC; ++c) acc[c] *= alpha;
+                for (int c = 0; c < EPC; ++c) acc[c] *= alpha;
+                m = mn;
+            }
+            const float mu = (m == kNegInf) ? 0.f : m;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const float p = fast_exp2(sc[u] - mu);
@@ -334,7 +359,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 }
                 chunk_axpy<CT>(vr[u], w, acc);
             }
-            m = mn;
         };
 
         // Even tiles live in buffer A, odd tiles in B.  The steady-state loop
@@ -368,7 +392,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         if constexpr (I8) {
             pw *= f;
 #pragma unroll
-            for (int c = 0; c < EPC; ++c) acc[c] -= 128.f * pw;
+            for (int c = 0; c < EPC; ++c) acc[c] -= kI8Offset * pw;
         }
         l = sum_over_slots<GP>(l);
 #pragma unroll
