@@ -110,10 +110,14 @@ typedef enum wsvd_status {
  *                               (-inf for an empty split).
  *   out, out_dt      [nb, nh, H] F32 | BF16 | F16, or NULL to stop after the
  *                    partials (e.g. to merge partials from several devices
- *                    with wsvd_combine_splits).  With an output the whole
- *                    step is one kernel launch: the last split of each
- *                    (b, h) to finish merges that row's partials (in split
- *                    order, so results do not depend on scheduling).
+ *                    with wsvd_combine_splits).  With an output and up to
+ *                    2047 split blocks (nb*nh*S) the whole step is one
+ *                    kernel launch: the last split of each (b, h) to finish
+ *                    merges that row's partials.  Larger grids write the
+ *                    partials and merge them in a second launch (the
+ *                    wsvd_combine_splits kernel).  Either way partials are
+ *                    merged in split order, so the result is the same and
+ *                    does not depend on scheduling.
  *   stream           HIP stream to enqueue on (0 = null stream).
  */
 int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap,
@@ -292,7 +296,7 @@ int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap,
  * wsvd_dense_decode_attn -- the speed baseline the pages compare WSVD with:
  * ordinary Flash-Decoding attention over full K and V (Japanese page
  * section 4, German page section 4: decode latency against Flash Decoding).
- * Same split rule, partial format, in-kernel merge and workspace as
+ * Same split rule, partial format, merge (in-kernel or second launch) and workspace as
  * wsvd_decode_attn; it exists so both can be timed on the same device.
  *
  *     out[b,h,:] = softmax(sigma * K[b,h,:l,:] q[b,h,:]) V[b,h,:l,:],  l = L[b]

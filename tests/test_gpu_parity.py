@@ -463,3 +463,29 @@ def test_dense_baseline_full_llava_layer(W):
     out = W.dense_decode_attn(d["q"], d["C_K"], d["C_V"], d["L"])
     torch.cuda.synchronize()
     check("dense llava layer", f64(out), O.decode_attn(inp), TOL["bf16"])
+
+
+def test_large_grid_merges_in_second_launch(W):
+    """64 x 8 heads x 4 splits = 2048 blocks: the partials are merged by the
+    merge kernel in a second launch.  Same result as the oracle, as the
+    stand-alone merge of the same partials, and as a one-launch grid."""
+    L = (np.arange(64, dtype=np.int32) * 37) % 300 + 1
+    inp = I.make_decode_inputs(64, 8, 64, 16, L, 300, seed=4100, act_dt="bf16", C_dt="bf16", q_gain=2.0 * 64)
+    out, o_part, lse = run_decode(W, inp, n_splits=4)
+    check("large grid S=4", f64(out), O.decode_attn(inp), TOL["bf16"])
+    merged = W.combine_splits(o_part.contiguous(), lse.contiguous(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out, merged)
+    small = I.make_decode_inputs(8, 8, 64, 16, L[:8], 300, seed=4100, act_dt="bf16", C_dt="bf16", q_gain=2.0 * 64)
+    out8, _, _ = run_decode(W, small, n_splits=4)          # 256 blocks: merged in-kernel
+    check("small grid S=4", f64(out8), O.decode_attn(small), TOL["bf16"])
+
+
+def test_dense_baseline_large_grid(W):
+    """2048 split blocks: the dense baseline also merges in a second launch."""
+    L = (np.arange(64, dtype=np.int32) * 37) % 300 + 1
+    inp = _dense_case(64, 8, 64, L, 300, seed=4200, q_gain=2.0 * 64)
+    d = W.device_inputs(inp)
+    out = W.dense_decode_attn(d["q"], d["C_K"], d["C_V"], d["L"], n_splits=4)
+    torch.cuda.synchronize()
+    check("dense large grid", f64(out), O.decode_attn(inp), TOL["bf16"])

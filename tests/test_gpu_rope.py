@@ -86,3 +86,11 @@ def test_rope_with_zero_angles_equals_folded_decode(W):
     ref = O.decode_attn(inp)
     assert rel(g, ref) <= TOL
     assert rel(g, folded.float().cpu().numpy().astype(np.float64)) <= TOL
+
+
+def test_rope_decode_large_grid(W):
+    """64 x 8 heads x 4 splits = 2048 blocks: partials merged in a second launch."""
+    L = (np.arange(64, dtype=np.int32) * 37) % 300 + 1
+    inp = I.make_decode_inputs(64, 8, 64, 32, L, 300, seed=1600, act_dt="bf16", C_dt="bf16", q_gain=4.0 * 64)
+    g, _ = run(W, inp, n_splits=4)
+    assert rel(g, O.decode_attn_rope(inp)) <= TOL
