@@ -527,7 +527,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep",
-                                       "factorize-loop", "shared-loop"],
+                                       "factorize-loop", "shared-loop", "rope-loop", "append-loop"],
                     default="bench",
                     help="decode-loop / step-loop / copy-calib / counters: plain launch loops for traces and counters")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
@@ -599,6 +599,54 @@ def main():
             del w
             torch.cuda.empty_cache()
         print(json.dumps(rec))
+        return
+    if args.mode == "rope-loop":
+        # Plain launch loop of the rotary-key decode (with output) on workload
+        # --config's buffers, for kernel traces.
+        cfg = CONFIGS[args.config]
+        w = Workload(cfg)
+        c, s_ = wsvd.rope_tables(cfg.L_cap, cfg.H)
+        calls = []
+        for d in w.sets:
+            out = torch.empty(cfg.nb, cfg.nh, cfg.H, dtype=d["q"].dtype, device="cuda")
+            ws = wsvd.decode_workspace(cfg.nb, cfg.nh, cfg.H, cfg.L_cap, 0)
+            calls.append(wsvd.PreparedDecodeRope(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], c, s_,
+                                                 workspace=ws, out=out))
+        for i in range(args.steps):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": args.mode, "workload": cfg.name, "launches": args.steps}))
+        return
+    if args.mode == "append-loop":
+        # Plain launch loops of the append at workload 5's shape: bf16 operands,
+        # then the W8A8 path (quantise x + integer append), --steps each.
+        cfg = CONFIGS[5]
+        nb, E, nh, r, L_cap = cfg.nb, cfg.E, cfg.nh, cfg.r, cfg.L_cap
+        N = nh * r
+        g = torch.Generator(device="cuda").manual_seed(0)
+        bf = torch.bfloat16
+        x = (torch.randn(nb, E, generator=g, device="cuda") * E ** -0.5).to(bf)
+        pos = torch.randint(0, L_cap, (nb,), generator=g, device="cuda", dtype=torch.int32)
+        C_K = torch.zeros(nb, nh, L_cap, r, dtype=bf, device="cuda")
+        C_V = torch.zeros_like(C_K)
+        ws = wsvd.append_workspace(nb, E, nh, r)
+        facs = []
+        for _ in range(8):
+            AK = (torch.randn(E, N, generator=g, device="cuda") * r ** -0.5).to(bf)
+            AV = (torch.randn(E, N, generator=g, device="cuda") * r ** -0.5).to(bf)
+            facs.append((wsvd.PreparedAppend(x, AK, AV, pos, C_K, C_V, workspace=ws),
+                         *wsvd.w8a8_prepare_factor(AK), *wsvd.w8a8_prepare_factor(AV)))
+        xq = torch.empty(nb, E, dtype=torch.int8, device="cuda")
+        sx = torch.empty(nb, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            facs[i % 8][0]()
+        for i in range(args.steps):
+            _, AKq, sAK, AVq, sAV = facs[i % 8]
+            wsvd.w8a8_quantize_activations(x, xq=xq, sx=sx)
+            wsvd.append_latent_w8a8(xq, sx, AKq, sAK, AVq, sAV, pos, C_K, C_V, workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": args.mode, "shape": f"x[{nb},{E}] -> {nh} heads x r {r}", "launches": args.steps}))
         return
     if args.mode == "shared-loop":
         # Plain launch loop of the shared-latent decode at the cache size of
