@@ -40,10 +40,17 @@ KERNEL_SOURCES = ("decode.hip", "wsvd_common.hpp", "split_merge.hpp")
 
 
 def kernel_src_hash() -> str:
+    """Hash of the split kernel's code: its sources with comments and blank
+    space removed, so that the counter summary stays valid across edits of
+    comments only."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "rank_kv_cache_flash_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "rank_kv_cache_flash_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -36,15 +36,20 @@
 // merge uses VALU cross-lane operations (DPP row rotations and the gfx950
 // permlane16/32 swaps), not LDS round trips.
 //
-// Merge: when an output is requested, each split stores its partial, then
-// the last split of a (b, h) to finish (a per-(b, h) counter in the
-// workspace, reset by that split) merges all of them in split order -- so
-// one launch does the whole step and the result is deterministic.
+// Merge: when an output is requested (and the grid is small enough for the
+// host to keep the merge in this launch), each split stores its partial,
+// then the last split of a (b, h) to finish (a per-(b, h) counter in the
+// workspace, reset by that split) merges all of them in split order, so the
+// result is deterministic.  Larger grids leave the merge to a second launch.
 //
-// int8 rows are converted with the byte-to-float instructions after an
-// xor with 0x80 (value = byte - 128); the -128 offset is folded into a
-// per-lane constant for the scores and into a running sum of weights for V,
-// so each code costs one convert and one FMA.
+// The online softmax moves its reference max only when a score passes it by
+// 2^8, so the accumulators are not rescaled on every tile.
+//
+// int8 rows: after an xor with 0x80, one byte permute turns two codes into
+// two exact fp16 values 1024 + 128 + code, and each code then costs one
+// mixed-precision FMA (fp16 operand, fp32 accumulate); the offset is folded
+// into a per-lane constant for the scores and into a running sum of weights
+// for V.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
 #include "split_merge.hpp"

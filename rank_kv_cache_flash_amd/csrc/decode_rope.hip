@@ -30,7 +30,7 @@
 //  * Values stay in latent space: the lane accumulates p c_V of its row and
 //    rank chunk (online softmax per lane), and the split's r-vector is
 //    projected through B_Vh once, as in the folded kernel.
-//  * Partials, workspace layout and the in-kernel merge are the folded
+//  * Partials, workspace layout and the merge are the folded
 //    kernel's.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
