@@ -489,3 +489,14 @@ def test_dense_baseline_large_grid(W):
     out = W.dense_decode_attn(d["q"], d["C_K"], d["C_V"], d["L"], n_splits=4)
     torch.cuda.synchronize()
     check("dense large grid", f64(out), O.decode_attn(inp), TOL["bf16"])
+
+
+@pytest.mark.parametrize("C_dt", ["bf16", "i8"])
+def test_long_context(W, C_dt):
+    """One sequence of 65536 tokens, 4 heads: the automatic rule gives 64
+    splits of 1024 tokens; a near-uniform and a peaked query."""
+    for gain in (1.0, 40.0 * 128):
+        inp = I.make_decode_inputs(1, 4, 128, 32, 65536, 65536, seed=4300, act_dt="bf16", C_dt=C_dt,
+                                   outlier_p=0.01 if C_dt == "i8" else 0.0, outlier_mul=20.0, q_gain=gain)
+        out, _, _ = run_decode(W, inp)
+        check(f"long context {C_dt} gain={gain}", f64(out), O.decode_attn(inp), TOL[C_dt])
