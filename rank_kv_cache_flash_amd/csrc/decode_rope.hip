@@ -144,6 +144,12 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
             s1[p] = (a.L_cap > 1) ? rsin[HH + 16 * p + rr] : 0.f;
         }
 
+        constexpr bool BREG = (KS == 1);  // r = 32: the factor fragments stay in registers
+        R16 breg[BREG ? NJ : 1];
+        if constexpr (BREG) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) breg[j].u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 8 * g]);
+        }
         float m = kNegInf, l = 0.f;
         float acc[8 * KS];
 #pragma unroll
@@ -158,7 +164,8 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     R16 bf;
-                    bf.u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 32 * ks + 8 * g]);
+                    if constexpr (BREG) bf = breg[j];
+                    else bf.u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 32 * ks + 8 * g]);
                     kt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks].b, bf.b, kt[j], 0, 0, 0);
                 }
             }
