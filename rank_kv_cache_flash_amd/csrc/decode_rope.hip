@@ -14,9 +14,11 @@
 // k of wave w starts at row 16 w + 64 k of the split), two tiles in flight.
 //  * K tile: v_mfma_f32_16x16x32_bf16 with the 16 latent rows as the A
 //    operand (lane l: row l % 16, 8 consecutive ranks at 8 (l / 16)), read
-//    straight from the cache, and B_Kh as the B operand, staged transposed
-//    in LDS.  The result (lane l: rows 4 (l / 16) .. +3, column l % 16 of
-//    each 16-column group) holds both members of every rotation pair
+//    straight from the cache, and B_Kh as the B operand: staged transposed
+//    in LDS once, then each lane keeps its fragments of the whole factor in
+//    registers for the split (r H / 512 u32x4 per lane), so tiles do not
+//    re-read LDS.  The result (lane l: rows 4 (l / 16) .. +3, column l % 16
+//    of each 16-column group) holds both members of every rotation pair
 //    (column c and c + H/2) in one lane.
 //  * Rotation: pair (c, c + H/2) of row t turns by t theta_c.  Since
 //    <q, R(t) k> = <R(-t) q, k>, the lane turns its slice of q instead: to
@@ -144,12 +146,12 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
             s1[p] = (a.L_cap > 1) ? rsin[HH + 16 * p + rr] : 0.f;
         }
 
-        constexpr bool BREG = (KS == 1);  // r = 32: the factor fragments stay in registers
-        R16 breg[BREG ? NJ : 1];
-        if constexpr (BREG) {
+        R16 breg[NJ * KS];  // this lane's B operand fragments of B_Kh
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) breg[j].u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 8 * g]);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                breg[ks * NJ + j].u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 32 * ks + 8 * g]);
         float m = kNegInf, l = 0.f;
         float acc[8 * KS];
 #pragma unroll
@@ -164,8 +166,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     R16 bf;
-                    if constexpr (BREG) bf = breg[j];
-                    else bf.u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 32 * ks + 8 * g]);
+                    bf = breg[ks * NJ + j];
                     kt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks].b, bf.b, kt[j], 0, 0, 0);
                 }
             }
