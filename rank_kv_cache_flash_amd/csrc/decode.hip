@@ -224,13 +224,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const uint32_t q_word = load_q_word(a.q, a.q_dt, q_idx);
     const char* bk_base = static_cast<const char*>(a.B_K) + (size_t)h * R * H * BES;
     const char* bv_base = static_cast<const char*>(a.B_V) + (size_t)h * R * H * BES;
+    // int8 caches: B_V (needed only after the token loop) is requested after
+    // the fold, so the first burst of requests -- which every block of the
+    // large int8 grids issues at once -- carries only q, B_K and latent tiles.
+    constexpr bool LATE_BV = I8;
     u32x4 bk[NBT], bv[NBT];
 #pragma unroll
     for (int k = 0; k < NBT; ++k) {
         const int c = tid + 256 * k;
         if (!DENSE && (NBC % 256 == 0 || c < NBC)) {
             bk[k] = *reinterpret_cast<const u32x4*>(bk_base + (size_t)c * 16);
-            bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
+            if constexpr (!LATE_BV) bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
         }
     }
 
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < BEPC; ++e) p = fmaf(chunk_elem<BT>(bk[k], e), sh_q[col + e], p);
                 sh_qpart[c] = p;
-                sh_bv[c] = bv[k];
+                if constexpr (!LATE_BV) sh_bv[c] = bv[k];
             }
         }
         __syncthreads();
@@ -320,6 +324,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < EPC; ++c) qoff += qp[c];
             qoff *= kI8Offset;
+        }
+
+        if constexpr (LATE_BV) {
+#pragma unroll
+            for (int k = 0; k < NBT; ++k) {
+                const int c = tid + 256 * k;
+                if (!DENSE && (NBC % 256 == 0 || c < NBC))
+                    bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
+            }
         }
 
         // ---- hot loop ----------------------------------------------------------
@@ -409,6 +422,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         if (lane == 0) {
             sh_red_m[wave] = Mw;
             sh_red_l[wave] = l;
+        }
+        if constexpr (LATE_BV) {
+#pragma unroll
+            for (int k = 0; k < NBT; ++k) {
+                const int c = tid + 256 * k;
+                if (!DENSE && (NBC % 256 == 0 || c < NBC)) sh_bv[c] = bv[k];
+            }
         }
         __syncthreads();
 
