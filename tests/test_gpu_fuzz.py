@@ -109,3 +109,28 @@ def test_shared_decode_random_shapes(W, seed):
     print(f"[parity] shared seed={seed}: {e:.3e}", flush=True)
     assert e <= TOL["bf16"]
     assert not got[L == 0].any()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_append_random_shapes(W, seed):
+    """Seeded random appends (bf16 and int8 caches), including out-of-range
+    positions, with the same checks as the fixed-shape append tests."""
+    from .test_gpu_parity import _append_case, _append_int8_case
+    g = np.random.default_rng(5600 + seed)
+    nb = int(g.integers(1, 71))
+    nh = int(g.integers(1, 9))
+    H = int(g.choice([64, 128]))
+    r = int(g.choice([16, 32, 48, 64]))
+    C_dt = str(g.choice(["bf16", "i8"]))
+    if C_dt == "i8" and r == 48:
+        r = 32
+    E = int(g.choice([256, 512, 1024, 2048, 4096]))
+    L_cap = int(g.integers(2, 60))
+    print(f"[case] append seed={seed} nb={nb} nh={nh} H={H} r={r} E={E} C={C_dt} L_cap={L_cap}", flush=True)
+    inp = I.make_ragged_step_inputs(nb, nh, H, r, E, 1, L_cap, L_cap, seed=5700 + seed, C_dt=C_dt)
+    if C_dt == "i8":
+        if nb > 1:
+            inp.pos[0] = L_cap      # out of range: skipped
+        _append_int8_case(W, inp)
+    else:
+        _append_case(W, inp)
