@@ -79,12 +79,15 @@ typedef enum wsvd_status {
  *
  * Arguments
  *   nb, nh, H, r     batch, heads, head dim, per-head rank (> 0, r <= H)
- *   L_cap            cache capacity in tokens (> 0)
+ *   L_cap            cache capacity in tokens (> 0); one sequence's rows of
+ *                    one head, L_cap * r elements, must stay below 2 GiB
+ *                    (WSVD_ERR_SHAPE otherwise)
  *   L                int32 [nb]: tokens attended per sequence.  Device
  *                    values are clamped to [0, L_cap]; L[b] == 0 yields a
  *                    zero output row.
  *   q, q_dt          [nb, nh, H]   F32 | BF16 | F16
- *   C_K, C_V, C_dt   [nb, nh, L_cap, r]   F32 | BF16 | I8
+ *   C_K, C_V, C_dt   [nb, nh, L_cap, r]   F32 | BF16 | I8.  Rows at or past
+ *                    L[b] may hold any bits: they are never read.
  *   s_K, s_V         fp16 [nb, nh, L_cap] per-token scales, required iff
  *                    C_dt == WSVD_I8 (value = code * scale); else ignored
  *   B_K, B_V, B_dt   [nh, r, H]    F32 | BF16 | F16
@@ -301,7 +304,7 @@ int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap,
  *
  *     out[b,h,:] = softmax(sigma * K[b,h,:l,:] q[b,h,:]) V[b,h,:l,:],  l = L[b]
  *
- *   K, V, kv_dt   [nb, nh, L_cap, H] BF16 (H in {64, 128})
+ *   K, V, kv_dt   [nb, nh, L_cap, H] BF16 (H in {64, 128}); L_cap * H below 2^30
  *   workspace     wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits)
  *                 bytes, counter area zero before first use (as above)
  *   other arguments as for wsvd_decode_attn.

@@ -34,6 +34,11 @@ bool act_dtype_ok(int dt) { return dt == WSVD_F32 || dt == WSVD_BF16 || dt == WS
 bool cache_dtype_ok(int dt) { return dt == WSVD_F32 || dt == WSVD_BF16 || dt == WSVD_I8; }
 bool head_dim_ok(int H) { return H == 64 || H == 128; }
 bool rank_ok(int r) { return r == 16 || r == 32 || r == 48 || r == 64; }
+// The split kernel addresses one (b, h)'s rows with 32-bit byte offsets.
+bool rows_fit(int L_cap, int row_elems, int dt) {
+    const long long es = dt == WSVD_F32 ? 4 : dt == WSVD_I8 ? 1 : 2;
+    return (long long)L_cap * row_elems * es < (1ll << 31);
+}
 
 int resolve_splits(int nb, int nh, int L_cap, int n_splits) {
     if (nb <= 0 || nh <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
@@ -128,6 +133,7 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, 
     if (!act_dtype_ok(q_dt) || !act_dtype_ok(B_dt) || !cache_dtype_ok(C_dt)) return WSVD_ERR_DTYPE;
     if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
     if (C_dt == WSVD_I8 && (!s_K || !s_V)) return WSVD_ERR_NULL;
+    if (!rows_fit(L_cap, r, C_dt)) return WSVD_ERR_SHAPE;
     if (!head_dim_ok(H) || !rank_ok(r)) return WSVD_ERR_UNSUPPORTED;
     if (!aligned16(L) || !aligned16(q) || !aligned16(C_K) || !aligned16(C_V) || !aligned16(B_K) ||
         !aligned16(B_V) || (out && !aligned16(out)))
@@ -180,6 +186,7 @@ int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap, const int32_t* L, c
     if (!L || !q || !K || !V) return WSVD_ERR_NULL;
     if (!act_dtype_ok(q_dt) || kv_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
     if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
+    if (!rows_fit(L_cap, H, kv_dt)) return WSVD_ERR_SHAPE;
     if (!head_dim_ok(H)) return WSVD_ERR_UNSUPPORTED;
     if (!aligned16(L) || !aligned16(q) || !aligned16(K) || !aligned16(V) || (out && !aligned16(out)))
         return WSVD_ERR_ALIGN;

@@ -31,11 +31,42 @@ __device__ __forceinline__ void merge_if_last_split(const DecodeArgs& a, size_t 
                    (unsigned)(S - 1));
     __syncthreads();
     if (!sh_last) return;
+    const float* lsp = a.lse_part + bh * S;
+    const float* opp = a.o_part + bh * S * H;
+    // Up to kFewSplits splits: every lane requests all lse values and its
+    // o_part column in one round trip, then sums in split order exactly as
+    // the chunked path below does for a single chunk.
+    constexpr int kFewSplits = 8;
+    if (S <= kFewSplits) {
+        if (tid < H) {
+            float lv[kFewSplits], ov[kFewSplits];
+#pragma unroll
+            for (int u = 0; u < kFewSplits; ++u) {
+                lv[u] = u < S ? load_coherent(lsp + u) : kNegInf;
+                ov[u] = u < S ? load_coherent(opp + (size_t)u * H + tid) : 0.f;
+            }
+            float M = kNegInf;
+#pragma unroll
+            for (int u = 0; u < kFewSplits; ++u) M = fmaxf(M, lv[u]);
+            float accm = 0.f, wsum = 0.f;
+            if (M != kNegInf) {
+#pragma unroll
+                for (int u = 0; u < kFewSplits; ++u) {
+                    if (u < S) {
+                        const float w = (lv[u] == kNegInf) ? 0.f : fast_exp2((lv[u] - M) * kLog2e);
+                        wsum += w;
+                        accm = fmaf(w, ov[u], accm);
+                    }
+                }
+            }
+            store_elem_wt(a.out, a.out_dt, bh * H + tid, wsum > 0.f ? accm / wsum : 0.f);
+        }
+        if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     // Online merge over chunks of up to 256 splits: one parallel load of the
     // chunk's lse values into LDS, then each output lane issues its o_part
     // loads eight at a time before consuming them.
-    const float* lsp = a.lse_part + bh * S;
-    const float* opp = a.o_part + bh * S * H;
     float Mrun = kNegInf, accm = 0.f, wsum = 0.f;
     for (int k0 = 0; k0 < S; k0 += 256) {
         const int n = min(256, S - k0);

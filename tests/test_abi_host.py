@@ -94,6 +94,9 @@ def decode(L, **kw):
     (dict(q=P + 8), EALIGN), (dict(C_K=P + 4), EALIGN), (dict(B_V=P + 2), EALIGN), (dict(out=P + 8), EALIGN),
     (dict(C_dt=I8, s_K=P, s_V=P + 2), EALIGN), (dict(Lp=P + 4), EALIGN),
     (dict(ws=None), EWS), (dict(ws_bytes=16), EWS), (dict(ws=P + 16), EWS),
+    # one (b, h)'s rows must stay below 2 GiB (32-bit row offsets in the kernel)
+    (dict(nh=1, r=64, L_cap=1 << 23), ESHAPE), (dict(nh=1, r=64, L_cap=(1 << 23) - 1), EWS),
+    (dict(nh=1, r=64, C_dt=I8, s_K=P, s_V=P, L_cap=1 << 25), ESHAPE),
 ])
 def test_decode_rejects(L, kw, want):
     assert decode(L, **kw) == want
@@ -166,6 +169,7 @@ def dense(L, **kw):
     (dict(H=96), EUNSUP), (dict(H=32), EUNSUP),
     (dict(V=P + 4), EALIGN), (dict(q=P + 2), EALIGN),
     ({}, EWS), (dict(ws=None), EWS),
+    (dict(nb=1, nh=1, L_cap=1 << 23), ESHAPE), (dict(nb=1, nh=1, L_cap=(1 << 23) - 1), EWS),
 ])
 def test_dense_rejects(L, kw, want):
     assert dense(L, **kw) == want

@@ -500,3 +500,29 @@ def test_long_context(W, C_dt):
                                    outlier_p=0.01 if C_dt == "i8" else 0.0, outlier_mul=20.0, q_gain=gain)
         out, _, _ = run_decode(W, inp)
         check(f"long context {C_dt} gain={gain}", f64(out), O.decode_attn(inp), TOL[C_dt])
+
+
+@pytest.mark.parametrize("C_dt", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("S", [None, 1, 3])
+def test_rows_past_length_may_hold_any_bits(W, C_dt, S):
+    """Cache rows at or past L[b] (and their int8 scales) filled with NaN bit
+    patterns: the result must equal the run on clean rows bit for bit."""
+    L = np.array([300, 5, 0, 130, 1], np.int32)
+    inp = I.make_decode_inputs(5, 4, 128, 32, L, 300, seed=4400, act_dt="f32" if C_dt == "f32" else "bf16",
+                               C_dt=C_dt, q_gain=4.0 * 128)
+    d = W.device_inputs(inp)
+    clean, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], s_K=d.get("s_K"),
+                                s_V=d.get("s_V"), n_splits=S)
+    torch.cuda.synchronize()
+    clean = clean.clone()
+    keys = ["C_K", "C_V"] + (["s_K", "s_V"] if C_dt == "i8" else [])
+    for k in keys:
+        u = d[k].view(torch.uint8).view(5, 4, 300, -1)
+        for b in range(5):
+            u[b, :, int(L[b]):, :] = 0xFF
+    poisoned, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], s_K=d.get("s_K"),
+                                   s_V=d.get("s_V"), n_splits=S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(poisoned).all()
+    assert torch.equal(poisoned, clean)
+    check(f"rows past L poisoned {C_dt} S={S}", f64(poisoned), O.decode_attn(inp), TOL[C_dt])
