@@ -87,7 +87,7 @@ typedef enum wsvd_status {
  *                    zero output row.
  *   q, q_dt          [nb, nh, H]   F32 | BF16 | F16
  *   C_K, C_V, C_dt   [nb, nh, L_cap, r]   F32 | BF16 | I8.  Rows at or past
- *                    L[b] may hold any bits: they are never read.
+ *                    L[b] may hold any bits: they never enter the result.
  *   s_K, s_V         fp16 [nb, nh, L_cap] per-token scales, required iff
  *                    C_dt == WSVD_I8 (value = code * scale); else ignored
  *   B_K, B_V, B_dt   [nh, r, H]    F32 | BF16 | F16

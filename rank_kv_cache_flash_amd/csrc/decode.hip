@@ -151,24 +151,15 @@ __device__ __forceinline__ void chunk_axpy(const u32x4& d, float w, float* acc) 
     }
 }
 
-// q element idx: the dword holding it (one unconditional load, any dtype)
-// and, separately, its value.  Converting only after every other prologue
-// request is out keeps the first requests from waiting on this one.
-__device__ __forceinline__ uint32_t load_q_word(const void* q, int q_dt, size_t idx) {
-    const size_t word = (q_dt == WSVD_F32) ? idx : (idx >> 1);
-    return static_cast<const uint32_t*>(q)[word];
-}
-__device__ __forceinline__ float q_word_value(uint32_t w, int q_dt, size_t idx) {
-    const uint16_t half = (idx & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
-    const float fb = bf16_to_f32(half);
-    const float fh = f16_to_f32(half);
-    return (q_dt == WSVD_F32) ? __uint_as_float(w) : (q_dt == WSVD_BF16 ? fb : fh);
-}
-
 // DENSE = true is the comparison baseline: ordinary Flash-Decoding over full
 // K / V rows (r = H, no factors): q' is q itself and the partial is o / l.
+//
+// Rank-48 instances are held to 3 waves per SIMD (3 resident blocks per CU):
+// measured on MI355X over the ragged 64 x 32-head step, a 4th resident block
+// per CU made the split kernel about 2.5 us slower.
 template <int H, int R, int CT, int BT, int U, bool DENSE = false>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, (R == 48) ? 3 : 8)))
+void decode_split_kernel(DecodeArgs a) {
     static_assert(!DENSE || R == H, "dense rows are H wide");
     using T = CacheTraits<CT>;
     constexpr int EPC = T::EPC;
@@ -188,7 +179,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     constexpr int NPART = 256 / H;                 // projection: threads per output
     static_assert(R % NPART == 0, "projection split");
 
-    __shared__ float sh_q[H];
+    __shared__ float sh_q[256];  // q in [0, H); every thread stores its word
     __shared__ float sh_qpart[NBC];
     __shared__ float sh_qp[R];
     __shared__ u32x4 sh_bv[NBC];
@@ -237,6 +228,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             if constexpr (!LATE_BV) bv[k] = *reinterpret_cast<const u32x4*>(bv_base + (size_t)c * 16);
         }
     }
+    // Keep the q and factor requests ahead of the latent tiles below.
+    __builtin_amdgcn_sched_barrier(0);
 
     ell = min(max(ell, 0), a.L_cap);
     const int chunk = (ell + S - 1) / S;
@@ -249,7 +242,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
     // No branch on ntok: every block runs the same code, so nothing keeps the
     // factor and q requests above from being issued before L[b] lands.  An
-    // empty range (ntok == 0) requests no latent tile and ends with a zero
+    // empty range (ntok == 0) consumes no latent tile and ends with a zero
     // partial and lse = -inf.
     {
         // ---- first latent batches ---------------------------------------------
@@ -257,11 +250,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const int j = lane % GP;
         const bool act = j < G;
         constexpr uint32_t row_bytes = (uint32_t)R * T::SZ;
-        const char* kbase = static_cast<const char*>(a.C_K) + (bh * a.L_cap + t0) * row_bytes;
-        const char* vbase = static_cast<const char*>(a.C_V) + (bh * a.L_cap + t0) * row_bytes;
-        const char* skb = I8 ? reinterpret_cast<const char*>(a.s_K + bh * a.L_cap + t0) : nullptr;
-        const char* svb = I8 ? reinterpret_cast<const char*>(a.s_V + bh * a.L_cap + t0) : nullptr;
+        const char* kseq = static_cast<const char*>(a.C_K) + bh * a.L_cap * row_bytes;
+        const char* vseq = static_cast<const char*>(a.C_V) + bh * a.L_cap * row_bytes;
+        const char* skseq = I8 ? reinterpret_cast<const char*>(a.s_K + bh * a.L_cap) : nullptr;
+        const char* svseq = I8 ? reinterpret_cast<const char*>(a.s_V + bh * a.L_cap) : nullptr;
         const uint32_t lane_off = (uint32_t)min(j, G - 1) * 16u;
+        // Requested rows are clamped to the split's last row (for an empty
+        // split: row t0, kept inside the cache), so every request is in bounds
+        // and rows past the split re-read valid data.  Offsets stay 32-bit:
+        // the host bounds L_cap * row bytes below 2^31.
+        const int rlast = min(t0 + max(ntok, 1) - 1, a.L_cap - 1);
 
         // int8 scales are kept as raw fp16 bits, one per 32-bit register:
         // two halves packed into one register would need the loads to land
@@ -272,27 +270,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         auto load_tile = [&](int tb, u32x4* kr, u32x4* vr, uint32_t* sk, uint32_t* sv) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t row = (uint32_t)min(tb + u * RW + g, ntok - 1);
+                const uint32_t row = (uint32_t)min(t0 + tb + u * RW + g, rlast);
                 const uint32_t off = row * row_bytes + lane_off;
-                kr[u] = load16_stream(kbase + off);
-                vr[u] = load16_stream(vbase + off);
+                kr[u] = load16_stream(kseq + off);
+                vr[u] = load16_stream(vseq + off);
                 if constexpr (I8) {  // raw fp16 bits: converted when consumed, so no wait here
-                    sk[u] = *reinterpret_cast<const uint16_t*>(skb + row * 2u);
-                    sv[u] = *reinterpret_cast<const uint16_t*>(svb + row * 2u);
+                    sk[u] = *reinterpret_cast<const uint16_t*>(skseq + row * 2u);
+                    sv[u] = *reinterpret_cast<const uint16_t*>(svseq + row * 2u);
                 }
             }
         };
 
         // This wave's tiles start at tb + k * STEP; the first two are requested
-        // before the prologue waits for anything.
+        // before the prologue waits for anything, unconditionally (a wave with
+        // fewer rows re-reads the split's last row): with a branch around them
+        // the waits for q and the factors below would have to assume the
+        // tiles were not requested and so wait for them as well.
         constexpr int STEP = NW * TILE;
         int tb = wave * TILE;
-        if (tb < ntok) load_tile(tb, kA, vA, skA, svA);
-        if (tb + STEP < ntok) load_tile(tb + STEP, kB, vB, skB, svB);
+        load_tile(tb, kA, vA, skA, svA);
+        load_tile(tb + STEP, kB, vB, skB, svB);
 
         // ---- q' = (sigma log2 e) B_K q from the chunks in registers ------------
         const float qv = q_word_value(q_word, a.q_dt, q_idx);
-        if (tid < H) sh_q[tid] = qv;
+        sh_q[tid] = qv;  // unconditional, so the q request is not sunk below the tiles
         if (DENSE && tid < H) sh_qp[tid] = qv * a.scale_log2;
         __syncthreads();
 #pragma unroll

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 
     __shared__ __attribute__((aligned(16))) uint16_t sBkT[H * BP];
     __shared__ u32x4 sh_bv[NBC];
-    __shared__ float sh_q[H];
+    __shared__ float sh_q[256];  // q in [0, H); every thread stores its value
     __shared__ float sh_red_o[NW][R];
     __shared__ float sh_red_m[NW];
     __shared__ float sh_red_l[NW];
@@ -86,18 +86,42 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
     const int S = a.S;
 
     int ell = a.L[b];
+
+    // q and both factors are requested first, ahead of the latent tiles, so
+    // that staging them below waits only for these requests.
+    static_assert(NBC % 256 == 0, "factor chunks per thread");
+    constexpr int NBT = NBC / 256;
+    const size_t bh = (size_t)b * a.nh + h;
+    const size_t q_idx = bh * H + (tid < H ? tid : 0);
+    const uint32_t q_word = load_q_word(a.q, a.q_dt, q_idx);
+    const u32x4* bkc = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.B_K) + (size_t)h * R * H);
+    const u32x4* bvc = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.B_V) + (size_t)h * R * H);
+    u32x4 bkr[NBT], bvr[NBT];
+#pragma unroll
+    for (int k = 0; k < NBT; ++k) {
+        bkr[k] = bkc[tid + 256 * k];
+        bvr[k] = bvc[tid + 256 * k];
+    }
+    float c1[NP], s1[NP];  // cos / sin of theta_c, c = 16 p + rr (table row 1)
+    const int row1 = (a.L_cap > 1) ? HH : 0;  // a one-row table: row 0 (angle 0)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        c1[p] = rcos[row1 + 16 * p + rr];
+        s1[p] = rsin[row1 + 16 * p + rr];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     ell = min(max(ell, 0), a.L_cap);
     const int chunk = (ell + S - 1) / S;
     const int t0 = min(ell, s * chunk);
     const int t1 = min(ell, t0 + chunk);
     const int ntok = t1 - t0;
 
-    const size_t bh = (size_t)b * a.nh + h;
     float* o_out = a.o_part + (bh * S + s) * H;
     float lse_out = kNegInf;
 
     if (ntok > 0) {  // uniform over the block
-        // ---- first two tiles of the wave, then q and the factors --------------------
+        // ---- first two tiles of the wave, then q and the factors staged ------------
         const uint16_t* kbase = static_cast<const uint16_t*>(a.C_K) + (bh * a.L_cap + t0) * R + 8 * g;
         const uint16_t* vbase = static_cast<const uint16_t*>(a.C_V) + (bh * a.L_cap + t0) * R + 8 * g;
 
@@ -119,32 +143,28 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
             }
         };
 
+        // Both tiles are requested unconditionally (a wave with fewer rows
+        // re-reads the split's last row): with a branch around them the waits
+        // for the factors below would also wait for the tiles.
         const int tb0 = wave * TR;
-        if (tb0 < ntok) load_tile(tb0, kA, vA, cA, sA);
-        if (tb0 + STEP < ntok) load_tile(tb0 + STEP, kB, vB, cB, sB);
+        load_tile(tb0, kA, vA, cA, sA);
+        load_tile(tb0 + STEP, kB, vB, cB, sB);
 
-        const uint16_t* bk = static_cast<const uint16_t*>(a.B_K) + (size_t)h * R * H;
-        const u32x4* bv = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.B_V) + (size_t)h * R * H);
-        for (int c = tid; c < NBC; c += 256) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(bk + (size_t)c * 8);
+#pragma unroll
+        for (int kk = 0; kk < NBT; ++kk) {
+            const int c = tid + 256 * kk;
             const int k = c / (H / 8);
             const int n0 = (c % (H / 8)) * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sBkT[(n0 + e) * BP + k] = uint16_t(v[e >> 1] >> ((e & 1) * 16));
-            sh_bv[c] = bv[c];
+            for (int e = 0; e < 8; ++e) sBkT[(n0 + e) * BP + k] = uint16_t(bkr[kk][e >> 1] >> ((e & 1) * 16));
+            sh_bv[c] = bvr[kk];
         }
-        if (tid < H) sh_q[tid] = load_elem(a.q, a.q_dt, bh * H + tid);
+        sh_q[tid] = q_word_value(q_word, a.q_dt, q_idx);
         __syncthreads();
 
         float qv[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) qv[j] = sh_q[16 * j + rr] * a.scale_log2;
-        float c1[NP], s1[NP];  // cos / sin of theta_c, c = 16 p + rr
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            c1[p] = (a.L_cap > 1) ? rcos[HH + 16 * p + rr] : 1.f;
-            s1[p] = (a.L_cap > 1) ? rsin[HH + 16 * p + rr] : 0.f;
-        }
 
         R16 breg[NJ * KS];  // this lane's B operand fragments of B_Kh
 #pragma unroll

@@ -45,6 +45,20 @@ __device__ __forceinline__ float load_elem(const void* p, int dt, size_t i) {
     }
 }
 
+// q element idx: the dword holding it (one unconditional load, any dtype)
+// and, separately, its value.  Converting only after every other prologue
+// request is out keeps the first requests from waiting on this one.
+__device__ __forceinline__ uint32_t load_q_word(const void* q, int q_dt, size_t idx) {
+    const size_t word = (q_dt == WSVD_F32) ? idx : (idx >> 1);
+    return static_cast<const uint32_t*>(q)[word];
+}
+__device__ __forceinline__ float q_word_value(uint32_t w, int q_dt, size_t idx) {
+    const uint16_t half = (idx & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
+    const float fb = bf16_to_f32(half);
+    const float fh = f16_to_f32(half);
+    return (q_dt == WSVD_F32) ? __uint_as_float(w) : (q_dt == WSVD_BF16 ? fb : fh);
+}
+
 // Store `v` as element i of a tensor of runtime dtype `dt`, written through
 // to memory at device scope.  Results a kernel leaves behind go out this
 // way: a plain store leaves a dirty L2 line for the end-of-kernel release
