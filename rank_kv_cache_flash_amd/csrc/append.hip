@@ -279,11 +279,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x4{0.f, 0.f, 0.f, 0.f};
         // Two stages (512 E rows) requested together; the split factor keeps
         // a block's slice at one or two stages, so one pass normally covers it.
-        for (int st = 0; st < ns; st += 2) {
+        // Pairs are requested without a branch between them (an odd last
+        // stage goes alone): behind a branch, the waits for the first stage
+        // would also wait for the second, so its MFMAs could not overlap the
+        // second stage's flight.
+        int st = 0;
+        for (; st + 1 < ns; st += 2) {
             load_stage(s0, c, e_beg + st * AP_EC);
-            if (st + 1 < ns) load_stage(s1, c, e_beg + (st + 1) * AP_EC);
+            load_stage(s1, c, e_beg + (st + 1) * AP_EC);
             mma_stage(s0, sB, sX, acc, tid, lane, wave);
-            if (st + 1 < ns) mma_stage(s1, sB, sX, acc, tid, lane, wave);
+            mma_stage(s1, sB, sX, acc, tid, lane, wave);
+        }
+        if (st < ns) {
+            load_stage(s0, c, e_beg + st * AP_EC);
+            mma_stage(s0, sB, sX, acc, tid, lane, wave);
         }
     } else {
         TileCtxW8 c;
@@ -300,11 +309,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         for (int jn = 0; jn < 4; ++jn) iacc[jn] = i32x4{0, 0, 0, 0};
         uint8_t* bB = reinterpret_cast<uint8_t*>(sB);
         uint8_t* bX = reinterpret_cast<uint8_t*>(sX);
-        for (int st = 0; st < ns; st += 2) {
+        int st = 0;
+        for (; st + 1 < ns; st += 2) {
             load_stage_w8(s0, c, e_beg + st * AP_ECB);
-            if (st + 1 < ns) load_stage_w8(s1, c, e_beg + (st + 1) * AP_ECB);
+            load_stage_w8(s1, c, e_beg + (st + 1) * AP_ECB);
             mma_stage_w8(s0, bB, bX, iacc, tid, lane, wave);
-            if (st + 1 < ns) mma_stage_w8(s1, bB, bX, iacc, tid, lane, wave);
+            mma_stage_w8(s1, bB, bX, iacc, tid, lane, wave);
+        }
+        if (st < ns) {
+            load_stage_w8(s0, c, e_beg + st * AP_ECB);
+            mma_stage_w8(s0, bB, bX, iacc, tid, lane, wave);
         }
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) acc[jn] = __builtin_bit_cast(f32x4, iacc[jn]);
