@@ -103,7 +103,9 @@ typedef enum wsvd_status {
  *                    every call leaves the counters at zero again.  Calls
  *                    in flight at the same time need separate workspaces.
  *                    On return (stream order) the workspace holds the split
- *                    partials:
+ *                    partials, except with an output and S == 1: then each
+ *                    row goes straight to out and the partial area is left
+ *                    as it was.  Partials:
  *                      o_part   float [nb, nh, S, H] at byte offset 0,
  *                               each split's attention normalised over its
  *                               own tokens (zeros for an empty split);

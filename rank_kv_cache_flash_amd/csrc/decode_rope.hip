@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 
     float* o_out = a.o_part + (bh * S + s) * H;
     float lse_out = kNegInf;
+    const bool direct = (S == 1) && a.out;  // one split with an output: no partial
 
     if (ntok > 0) {  // uniform over the block
         // ---- first two tiles of the wave, then q and the factors staged ------------
@@ -311,19 +312,26 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
             float o = 0.f;
 #pragma unroll
             for (int p = 0; p < NPART; ++p) o += sh_proj[p * H + tid];
-            store_coherent(o_out + tid, o);
-            if (S == 1 && a.out) store_elem_wt(a.out, a.out_dt, bh * H + tid, o);
+            if (direct) {
+                store_elem_wt(a.out, a.out_dt, bh * H + tid, o);
+            } else {
+                store_coherent(o_out + tid, o);
+            }
         }
         lse_out = (M + fast_log2(Lt)) * kLn2;
     } else {
         for (int i = tid; i < H; i += 256) {
-            store_coherent(o_out + i, 0.f);
-            if (S == 1 && a.out) store_elem_wt(a.out, a.out_dt, bh * H + i, 0.f);
+            if (direct) {
+                store_elem_wt(a.out, a.out_dt, bh * H + i, 0.f);
+            } else {
+                store_coherent(o_out + i, 0.f);
+            }
         }
     }
+    if (direct) return;
     if (tid == 0) store_coherent(a.lse_part + bh * S + s, lse_out);
 
-    if (!a.out || S == 1) return;
+    if (!a.out) return;
     merge_if_last_split<H>(a, bh, S, sh_proj, sh_last);
 }
 

@@ -159,7 +159,9 @@ def decode_attn(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=N
     q [nb, nh, H]; C_K / C_V [nb, nh, L_cap, r]; B_K / B_V [nh, r, H];
     L int32 [nb] (device); s_K / s_V fp16 [nb, nh, L_cap] for int8 caches.
     Returns out [nb, nh, H] (or None with partials_only) and the partial
-    views (o_part [nb, nh, S, H], lse_part [nb, nh, S]) inside workspace.
+    views (o_part [nb, nh, S, H], lse_part [nb, nh, S]) inside workspace;
+    with an output and one split the kernel writes out directly and leaves
+    those views unwritten.
     """
     for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"),
                  (s_K, "s_K"), (s_V, "s_V"), (out, "out"), (workspace, "workspace")):
