@@ -386,7 +386,8 @@ void decode_split_kernel(DecodeArgs a) {
 
         // Even tiles live in buffer A, odd tiles in B.  The steady-state loop
         // consumes a pair and requests the next pair unconditionally; the tail
-        // requests only tiles that exist, so nothing is left in flight.
+        // requests only tiles that exist (only the first pair may hold rows
+        // nobody consumes).
         const int nt = (ntok > tb) ? (ntok - tb + STEP - 1) / STEP : 0;
         int k = 0;
         // The scheduling barriers pin each refill between the two consumes:

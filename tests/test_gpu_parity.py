@@ -139,6 +139,29 @@ def test_merge_counters_reset_and_reuse(W):
     check("config 2 reused workspace", f64(outs[0]), ref, TOL["bf16"])
 
 
+def test_one_split_with_output_leaves_partials_alone(W):
+    """S = 1 with an output: rows go straight to out and the partial area of the
+    workspace keeps whatever it held (here a NaN fill); the output equals the
+    partials-only run's o_part, rounded once."""
+    L = np.array([300, 1, 0, 257], np.int32)
+    inp = I.make_decode_inputs(4, 3, 128, 32, L, 300, seed=4500, act_dt="bf16", C_dt="bf16", q_gain=4.0 * 128)
+    d = W.device_inputs(inp)
+    nb, nh, H = inp.q.shape
+    need = W.decode_workspace_bytes(nb, nh, H, inp.L_cap, 1)
+    off = W.decode_counter_offset(nb, nh, H, inp.L_cap, 1)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[off:] = 0
+    out, _, _ = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], n_splits=1, workspace=ws,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert bool((ws[:off] == 0xFF).all()), "partials must not be written with S = 1 and an output"
+    _, o_part, lse = W.decode_attn(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], n_splits=1,
+                                   partials_only=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_part[:, :, 0, :])
+    check("one split, direct output", f64(out), O.decode_attn(inp), TOL["bf16"])
+
+
 # ---------------------------------------------------------------------------
 # small cases spanning several tiles, ragged tails, every (H, r, cache dtype)
 # ---------------------------------------------------------------------------
