@@ -549,3 +549,46 @@ def test_rows_past_length_may_hold_any_bits(W, C_dt, S):
     assert torch.isfinite(poisoned).all()
     assert torch.equal(poisoned, clean)
     check(f"rows past L poisoned {C_dt} S={S}", f64(poisoned), O.decode_attn(inp), TOL[C_dt])
+
+
+@pytest.mark.parametrize("C_dt", ["f32", "bf16"])
+def test_largest_row_offsets(W, C_dt):
+    """One head whose cache rows end just below 2 GiB, the most the host
+    accepts for one sequence (the kernel's row offsets are 32-bit).  All rows
+    are zero except two marked ones, at a third of the cache and at its last
+    row; q points at the last marked key (score 30).  Expected: the oracle's
+    attention over the two marked rows merged with the zero rows (score 0,
+    value 0, log-sum-exp log(count))."""
+    H = r = 64
+    es = 4 if C_dt == "f32" else 2
+    L_cap = (1 << 31) // (r * es) - 1
+    act = "f32" if C_dt == "f32" else "bf16"
+    small = I.make_decode_inputs(1, 1, H, r, 2, 2, seed=4600, act_dt=act, C_dt=C_dt)
+    from oracle import wsvd_oracle as WO
+    sig = WO._sigma(H, None)
+    K = WO.reconstruct(WO.dequant_latent(small.C_K[0, 0], small.C_dt), WO.upcast(small.B_K[0], small.B_dt))
+    V = WO.reconstruct(WO.dequant_latent(small.C_V[0, 0], small.C_dt), WO.upcast(small.B_V[0], small.B_dt))
+    qd = 30.0 / sig * K[1] / float(K[1] @ K[1])
+    small.q[0, 0] = WO.round_to_bf16_bits(qd) if act == "bf16" else qd.astype(np.float32)
+    q = WO.upcast(small.q[0, 0], small.q_dt)
+    o_m, lse_m = WO.segment_attend(q, K, V, sig, 0, 2)
+    ref = WO.combine(np.stack([o_m, np.zeros(H)]), np.array([lse_m, math.log(L_cap - 2)]))
+
+    d = W.device_inputs(small)
+    pos = [L_cap // 3, L_cap - 1]
+    print(f"[case] largest offsets {C_dt}: L_cap={L_cap}, marked rows {pos}", flush=True)
+    C_K = torch.zeros((1, 1, L_cap, r), dtype=d["C_K"].dtype, device="cuda")
+    C_V = torch.zeros_like(C_K)
+    for i, p in enumerate(pos):
+        C_K[0, 0, p] = d["C_K"][0, 0, i]
+        C_V[0, 0, p] = d["C_V"][0, 0, i]
+    L = torch.tensor([L_cap], dtype=torch.int32, device="cuda")
+    outs = []
+    for S in (None, 3):
+        out, _, _ = W.decode_attn(d["q"], C_K, C_V, d["B_K"], d["B_V"], L, n_splits=S, out_dtype=torch.float32)
+        outs.append(out)
+    torch.cuda.synchronize()
+    del C_K, C_V
+    torch.cuda.empty_cache()
+    for S, out in zip((None, 3), outs):
+        check(f"largest row offsets {C_dt} S={S}", f64(out)[0, 0], ref, TOL[C_dt])
