@@ -30,17 +30,21 @@
 // tiles that exist.  Loads use a wave-uniform 64-bit base plus a 32-bit lane
 // offset (the scalar-base load form).
 //
-// Prologue: q, both factors and the first latent tiles are requested before
-// anything waits.  q' = B_K q is formed from the factor chunks held in
-// registers; B_V stays in LDS for the projection at the end.  The in-wave
-// merge uses VALU cross-lane operations (DPP row rotations and the gfx950
-// permlane16/32 swaps), not LDS round trips.
+// Prologue: q and both factors, then the first two latent tiles of every
+// wave, are requested before anything waits, all without a branch: vector
+// loads complete in order, so a wait for q placed after a conditional tile
+// request would also wait for the tiles.  q' = B_K q is formed from the
+// factor chunks held in registers while the tiles are in flight; B_V stays in
+// LDS for the projection at the end.  The in-wave merge uses VALU cross-lane
+// operations (DPP row rotations and the gfx950 permlane16/32 swaps), not LDS
+// round trips.
 //
-// Merge: when an output is requested (and the grid is small enough for the
-// host to keep the merge in this launch), each split stores its partial,
-// then the last split of a (b, h) to finish (a per-(b, h) counter in the
-// workspace, reset by that split) merges all of them in split order, so the
-// result is deterministic.  Larger grids leave the merge to a second launch.
+// Merge: with one split and an output the block writes out directly.  With
+// more splits and an output (and a grid small enough for the host to keep
+// the merge in this launch), each split stores its partial, then the last
+// split of a (b, h) to finish (a per-(b, h) counter in the workspace, reset
+// by that split) merges all of them in split order, so the result is
+// deterministic.  Larger grids leave the merge to a second launch.
 //
 // The online softmax moves its reference max only when a score passes it by
 // 2^8, so the accumulators are not rescaled on every tile.

@@ -32,8 +32,11 @@
 //  * Values stay in latent space: the lane accumulates p c_V of its row and
 //    rank chunk (online softmax per lane), and the split's r-vector is
 //    projected through B_Vh once, as in the folded kernel.
-//  * Partials, workspace layout and the merge are the folded
-//    kernel's.
+//  * Prologue: q, both factors and the cos / sin of one position step are
+//    requested first, then the wave's first two tiles without a branch, so
+//    staging B_Kh into LDS overlaps the tiles' flight.
+//  * Partials, workspace layout and the merge are the folded kernel's (with
+//    one split and an output, out is written directly).
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
 #include "split_merge.hpp"
