@@ -21,16 +21,40 @@ __global__ __launch_bounds__(256) void combine_kernel(int nbh, int H, int S, con
     const int t = threadIdx.x % H;
     if (row >= nbh) return;
     const float* ls = lse_part + (size_t)row * S;
+    const float* op = o_part + (size_t)row * S * H + t;
     float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ls[s]);
     float acc = 0.f, wsum = 0.f;
-    if (M != kNegInf) {
-        const float* op = o_part + (size_t)row * S * H + t;
-        for (int s = 0; s < S; ++s) {
-            const float lv = ls[s];
-            const float w = (lv == kNegInf) ? 0.f : fast_exp2((lv - M) * kLog2e);
-            wsum += w;
-            acc = fmaf(w, op[(size_t)s * H], acc);
+    constexpr int kFew = 8;
+    if (S <= kFew) {
+        // Every lse value and this lane's o_part column requested at once (one
+        // round trip); the sum below runs in the same order as the loop form.
+        float lv[kFew], ov[kFew];
+#pragma unroll
+        for (int s = 0; s < kFew; ++s) {
+            lv[s] = s < S ? ls[s] : kNegInf;
+            ov[s] = s < S ? op[(size_t)s * H] : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kFew; ++s) M = fmaxf(M, lv[s]);
+        if (M != kNegInf) {
+#pragma unroll
+            for (int s = 0; s < kFew; ++s) {
+                if (s < S) {
+                    const float w = (lv[s] == kNegInf) ? 0.f : fast_exp2((lv[s] - M) * kLog2e);
+                    wsum += w;
+                    acc = fmaf(w, ov[s], acc);
+                }
+            }
+        }
+    } else {
+        for (int s = 0; s < S; ++s) M = fmaxf(M, ls[s]);
+        if (M != kNegInf) {
+            for (int s = 0; s < S; ++s) {
+                const float lv = ls[s];
+                const float w = (lv == kNegInf) ? 0.f : fast_exp2((lv - M) * kLog2e);
+                wsum += w;
+                acc = fmaf(w, op[(size_t)s * H], acc);
+            }
         }
     }
     const float v = (wsum > 0.f) ? acc / wsum : 0.f;
