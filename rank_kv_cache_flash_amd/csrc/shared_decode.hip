@@ -264,13 +264,29 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(int nb, int nh, int S
     const int nbg = min(kMergeSeqs, nb - b0);
     const int k0 = c * kMergeRows;
 
+    // B_V rows of this chunk for the projection, requested first.
+    static_assert(kMergeRows % NKL == 0, "projection rows per thread");
+    const int cg = tid % GL, kl = tid / GL;
+    const size_t ld = (size_t)nh * H;
+    u32x4 bvr[kMergeRows / NKL];
+#pragma unroll
+    for (int it = 0; it < kMergeRows / NKL; ++it)
+        bvr[it] = *reinterpret_cast<const u32x4*>(B_V + (size_t)(k0 + kl + it * NKL) * ld + (size_t)h * H + cg * 8);
+
     for (int u = 0; u < kMergeSeqs; ++u) {
         float acc = 0.f, wsum = 0.f;
         if (u < nbg) {
             const size_t bh = (size_t)(b0 + u) * nh + h;
             const float* lsp = lse_part + bh * S;
+            // Loads eight at a time, issued before any is used.
             float Mx = kNegInf;
-            for (int s = 0; s < S; ++s) Mx = fmaxf(Mx, lsp[s]);
+            for (int s0 = 0; s0 < S; s0 += 8) {
+                float lv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lv[i] = s0 + i < S ? lsp[s0 + i] : kNegInf;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) Mx = fmaxf(Mx, lv[i]);
+            }
             for (int s0 = 0; s0 < S; s0 += 64) {
                 const int n = min(64, S - s0);
                 __syncthreads();
@@ -280,10 +296,19 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(int nb, int nh, int S
                 }
                 __syncthreads();
                 if (tid < kMergeRows) {
-                    for (int s = 0; s < n; ++s) {
-                        const float w = sh_w[s];
-                        wsum += w;
-                        acc = fmaf(w, o_part[(bh * S + s0 + s) * R + k0 + tid], acc);
+                    for (int s1 = 0; s1 < n; s1 += 8) {
+                        float ov[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            ov[i] = s1 + i < n ? o_part[(bh * S + s0 + s1 + i) * R + k0 + tid] : 0.f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            if (s1 + i < n) {
+                                const float w = sh_w[s1 + i];
+                                wsum += w;
+                                acc = fmaf(w, ov[i], acc);
+                            }
+                        }
                     }
                 }
             }
@@ -292,15 +317,18 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(int nb, int nh, int S
     }
     __syncthreads();
 
-    const int cg = tid % GL, kl = tid / GL;
-    const size_t ld = (size_t)nh * H;
     float o[kMergeSeqs][8];
 #pragma unroll
     for (int u = 0; u < kMergeSeqs; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[u][e] = 0.f;
-    for (int k = kl; k < kMergeRows; k += NKL) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(B_V + (size_t)(k0 + k) * ld + (size_t)h * H + cg * 8);
+    // This thread's kMergeRows / NKL rows of B_V, all requested before any is
+    // used (the chunk's B_V was also requested before the merge above).
+    constexpr int NIT = kMergeRows / NKL;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int k = kl + it * NKL;
+        const u32x4 bv = bvr[it];
 #pragma unroll
         for (int u = 0; u < kMergeSeqs; ++u) {
             const float ov = sh_o[u][k];
@@ -340,8 +368,14 @@ __global__ __launch_bounds__(256) void shared_sum_kernel(long n, int nc, const f
                                                          void* out, int out_dt) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
+    // nc <= 16 (R / 128): every contribution requested at once, summed in order.
+    float pv[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) pv[c] = c < nc ? proj_part[(size_t)c * n + i] : 0.f;
     float v = 0.f;
-    for (int c = 0; c < nc; ++c) v += proj_part[(size_t)c * n + i];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        if (c < nc) v += pv[c];
     store_elem_wt(out, out_dt, (size_t)i, v);
 }
 
