@@ -1,8 +1,8 @@
 """Seeded random shapes across the supported space, every output element
 against the fp64 oracle: the folded decode (all cache and activation dtypes,
-split counts, output dtypes, softmax scales), the rotary-key decode and the
-shared-latent decode.  Each case is drawn from its own seed and printed
-before it runs."""
+split counts, output dtypes, softmax scales), the rotary-key decode, the
+shared-latent decode, the dense baseline and the append.  Each case is drawn
+from its own seed and printed before it runs."""
 import numpy as np
 import pytest
 
@@ -134,3 +134,28 @@ def test_append_random_shapes(W, seed):
         _append_int8_case(W, inp)
     else:
         _append_case(W, inp)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_dense_random_shapes(W, seed):
+    """The Flash-Decoding baseline over full bf16 K / V on seeded random shapes:
+    the oracle with r = H and identity factors (pinned against library SDPA)."""
+    from .test_gpu_parity import _dense_case
+    g = np.random.default_rng(5800 + seed)
+    H = int(g.choice([64, 128]))
+    nb, nh = int(g.integers(1, 7)), int(g.integers(1, 9))
+    L_cap = int(g.integers(1, 700))
+    L = draw_lengths(g, nb, L_cap)
+    S = [None, 1, 2, 5][int(g.integers(0, 4))]
+    S = None if S is not None and S > L_cap else S
+    gain = float(g.choice([1.0, 4.0 * H]))
+    print(f"[case] dense seed={seed} H={H} nb={nb} nh={nh} L_cap={L_cap} S={S} gain={gain}", flush=True)
+    inp = _dense_case(nb, nh, H, L, L_cap, seed=5900 + seed, q_gain=gain)
+    d = W.device_inputs(inp)
+    out = W.dense_decode_attn(d["q"], d["C_K"], d["C_V"], d["L"], n_splits=S)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    e = rel(got, O.decode_attn(inp))
+    print(f"[parity] dense seed={seed}: {e:.3e}", flush=True)
+    assert e <= TOL["bf16"]
+    assert not got[L == 0].any()
