@@ -159,3 +159,19 @@ def test_dense_random_shapes(W, seed):
     print(f"[parity] dense seed={seed}: {e:.3e}", flush=True)
     assert e <= TOL["bf16"]
     assert not got[L == 0].any()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_append_w8a8_random_shapes(W, seed):
+    """Seeded random W8A8 appends (int8 activations and factors, bf16 or int8
+    caches), with the exact-code checks of the fixed-shape W8A8 tests."""
+    from .test_gpu_w8a8 import _w8_case
+    g = np.random.default_rng(6000 + seed)
+    nb = int(g.integers(1, 81))
+    nh = int(g.integers(1, 9))
+    C_dt = str(g.choice(["bf16", "i8"]))
+    r = int(g.choice([16, 32, 64] if C_dt == "i8" else [16, 32, 48, 64]))
+    E = int(g.choice([512, 1024, 1536, 2048, 2560, 4096]))
+    L_cap = int(g.integers(2, 40))
+    print(f"[case] w8a8 append seed={seed} nb={nb} nh={nh} r={r} E={E} C={C_dt} L_cap={L_cap}", flush=True)
+    _w8_case(W, nb, E, nh, r, C_dt, seed=6100 + seed, L_cap=L_cap)
