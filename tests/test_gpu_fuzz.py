@@ -1,8 +1,8 @@
 """Seeded random shapes across the supported space, every output element
 against the fp64 oracle: the folded decode (all cache and activation dtypes,
 split counts, output dtypes, softmax scales), the rotary-key decode, the
-shared-latent decode, the dense baseline and the append.  Each case is drawn
-from its own seed and printed before it runs."""
+shared-latent decode, the dense baseline, the appends and the stand-alone
+merge.  Each case is drawn from its own seed and printed before it runs."""
 import numpy as np
 import pytest
 
@@ -175,3 +175,30 @@ def test_append_w8a8_random_shapes(W, seed):
     L_cap = int(g.integers(2, 40))
     print(f"[case] w8a8 append seed={seed} nb={nb} nh={nh} r={r} E={E} C={C_dt} L_cap={L_cap}", flush=True)
     _w8_case(W, nb, E, nh, r, C_dt, seed=6100 + seed, L_cap=L_cap)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_combine_random_shapes(W, seed):
+    """wsvd_combine_splits on seeded random partials (split counts on both
+    sides of the one-round-trip path, empty splits with lse = -inf, whole rows
+    of empty splits) against the oracle's merge, fp32 output."""
+    g = np.random.default_rng(6200 + seed)
+    H = int(g.choice([64, 128]))
+    nb, nh = int(g.integers(1, 9)), int(g.integers(1, 9))
+    S = [1, 2, 3, 5, 8, 9, 64, 300][seed]      # both sides of the eight-split path
+    o = g.standard_normal((nb, nh, S, H)).astype(np.float32)
+    lse = (g.standard_normal((nb, nh, S)) * 20.0).astype(np.float32)
+    empty = g.random((nb, nh, S)) < 0.2
+    lse[empty] = -np.inf
+    o[empty] = 0.0
+    lse[0, 0, :] = -np.inf                       # one row with every split empty
+    o[0, 0] = 0.0
+    print(f"[case] combine seed={seed} H={H} nb={nb} nh={nh} S={S}", flush=True)
+    out = W.combine_splits(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = np.stack([np.stack([O.combine(o[b, h], lse[b, h]) for h in range(nh)]) for b in range(nb)])
+    e = rel(got, ref)
+    print(f"[parity] combine seed={seed}: {e:.3e}", flush=True)
+    assert e <= TOL["f32"]
+    assert not got[0, 0].any()
