@@ -371,6 +371,7 @@ int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap, const int8_
                                        workspace_bytes, 512);
     if (st != WSVD_OK) return st;
     wsvd::AppendArgs a = append_args(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace);
+    a.KS = wsvd::append_num_esplits_w8(nb, E, nh, r);
     a.w8 = 1;
     a.x = xq;
     a.sx = sx;

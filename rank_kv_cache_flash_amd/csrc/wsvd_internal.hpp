@@ -76,6 +76,8 @@ int w8a8_prepare_cols(int E);
 
 // Split-E factor the append kernel uses for these sizes (host).
 int append_num_esplits(int nb, int E, int nh, int r);
+// The int8-operand variant's split (never more slices than the one above).
+int append_num_esplits_w8(int nb, int E, int nh, int r);
 // Output tiles (64 rows x 64 columns, K and V separately) (host).
 long append_num_tiles(int nb, int nh, int r);
 // Bytes of split-E partial tiles for these sizes, 0 when KS == 1 (host).
