@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fused low-rank decode attn: µs/step and achieved HBM GB/s (% of peak), 1 GPU"
 COLD_BYTES = 1 << 30      # rotate input copies until >= 1 GiB is touched
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ("decode.hip", "wsvd_common.hpp", "split_merge.hpp")
+KERNEL_SOURCES = ("decode.hip", "decode_bf16_r32.hip", "wsvd_common.hpp", "split_merge.hpp")
 
 
 def kernel_src_hash() -> str:
@@ -51,6 +51,9 @@ def kernel_src_hash() -> str:
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
         h.update(" ".join(src.split()).encode())
+    from rank_kv_cache_flash_amd.build import SOURCE_FLAGS      # per-file compiler options change the code too
+    for f in KERNEL_SOURCES:
+        h.update(" ".join(SOURCE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -520,7 +520,10 @@ template <int H, int R>
 static hipError_t launch_hr(const DecodeArgs& a, int C_dt, hipStream_t st) {
     switch (C_dt) {
         case WSVD_F32: return launch_hrc<H, R, WSVD_F32>(a, st);
-        case WSVD_BF16: return launch_hrc<H, R, WSVD_BF16>(a, st);
+        case WSVD_BF16:
+            // The bf16 rank-32 instances live in decode_bf16_r32.hip.
+            if constexpr (R == 32) return launch_decode_bf16_r32(a, H, st);
+            else return launch_hrc<H, R, WSVD_BF16>(a, st);
         case WSVD_I8: return launch_hrc<H, R, WSVD_I8>(a, st);
         default: return hipErrorInvalidValue;
     }
@@ -537,6 +540,17 @@ static hipError_t launch_h(const DecodeArgs& a, int r, int C_dt, hipStream_t st)
     }
 }
 
+#ifdef WSVD_DECODE_BF16_R32_UNIT
+// The bf16-cache, rank-32 instances (every factor dtype, H 64 and 128),
+// compiled in a translation unit of their own; see decode_bf16_r32.hip.
+hipError_t launch_decode_bf16_r32(const DecodeArgs& a, int H, hipStream_t st) {
+    switch (H) {
+        case 64: return launch_hrc<64, 32, WSVD_BF16>(a, st);
+        case 128: return launch_hrc<128, 32, WSVD_BF16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+#else
 hipError_t launch_dense_split(const DecodeArgs& a, int H, hipStream_t st) {
     const unsigned nblk = (unsigned)((size_t)a.nb * a.nh * a.S);
     switch (H) {
@@ -561,5 +575,6 @@ hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipS
         default: return hipErrorInvalidValue;
     }
 }
+#endif
 
 }  // namespace wsvd

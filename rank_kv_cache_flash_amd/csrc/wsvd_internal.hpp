@@ -30,6 +30,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, int H, int r, int C_dt, hipStream_t st);
+// The bf16-cache, rank-32 split-kernel instances (decode_bf16_r32.hip).
+hipError_t launch_decode_bf16_r32(const DecodeArgs& a, int H, hipStream_t st);
 
 // Decode with a rotary position step on every reconstructed key row
 // (bf16 caches and factors; H in 64, 128; r in 32, 64).
