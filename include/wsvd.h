@@ -96,23 +96,36 @@ typedef enum wsvd_status {
  *                    wsvd_decode_num_splits).  Split s of a sequence with
  *                    l tokens covers [s*ceil(l/S), min(l, (s+1)*ceil(l/S))).
  *   workspace        device scratch of at least wsvd_decode_workspace_bytes
- *                    bytes, 256-byte aligned.  Its counter area (byte
- *                    offset wsvd_decode_counter_offset(...), nb*nh uint32)
- *                    must be zero before the first call that passes an
- *                    output -- allocate the workspace zero-filled once;
- *                    every call leaves the counters at zero again.  Calls
- *                    in flight at the same time need separate workspaces.
- *                    On return (stream order) the workspace holds the split
- *                    partials, except with an output and S == 1: then each
- *                    row goes straight to out and the partial area is left
- *                    as it was.  Partials:
- *                      o_part   float [nb, nh, S, H] at byte offset 0,
- *                               each split's attention normalised over its
- *                               own tokens (zeros for an empty split);
+ *                    bytes, 256-byte aligned.  Layout, each region 256-byte
+ *                    aligned:
+ *                      counters uint32 [nb, nh] at byte offset 0, in the
+ *                               first wsvd_decode_counter_bytes(nb, nh)
+ *                               bytes (same place for every split count);
+ *                      o_part   float [nb, nh, S, H] at byte offset
+ *                               wsvd_decode_opart_offset(...): each split's
+ *                               attention normalised over its own tokens
+ *                               (zeros for an empty split);
  *                      lse_part float [nb, nh, S] at byte offset
  *                               wsvd_decode_lse_offset(...): natural-log
  *                               log-sum-exp of the split's scaled scores
  *                               (-inf for an empty split).
+ *                    Zero-counter rule: when a call that passes an output
+ *                    starts, the counter bytes [0, wsvd_decode_counter_bytes
+ *                    (nb, nh)) must be zero, and the call leaves them zero;
+ *                    bytes past them need no initial contents and may be
+ *                    overwritten.  So a workspace zero-filled once serves
+ *                    any run of calls in stream order whose nb * nh never
+ *                    grows (a call with a larger nb * nh than an earlier one
+ *                    needs its counter bytes zero-filled again first).  The
+ *                    library cannot check this: with non-zero counters the
+ *                    last-split test misfires, so rows of out may be left
+ *                    unwritten or merged from partials that are not yet
+ *                    complete, and no error is returned.  Calls in flight at
+ *                    the same time need separate workspaces.  On return
+ *                    (stream order) the workspace holds the split partials,
+ *                    except with an output and S == 1: then each row goes
+ *                    straight to out and the partial area is left as it
+ *                    was.
  *   out, out_dt      [nb, nh, H] F32 | BF16 | F16, or NULL to stop after the
  *                    partials (e.g. to merge partials from several devices
  *                    with wsvd_combine_splits).  With an output and up to
@@ -187,13 +200,17 @@ int wsvd_combine_splits(int nb, int nh, int H, int n_splits,
  *   s_K, s_V         fp16 [nb, nh, L_cap] row scales, required (16-byte
  *                    aligned) iff C_dt == WSVD_I8; must be NULL otherwise
  *   workspace        device scratch of wsvd_append_workspace_bytes(...)
- *                    bytes, 256-byte aligned: fp32 split-E partial tiles
- *                    and one arrival counter per output tile.  It must be
- *                    zero-filled before its first use; every call leaves
- *                    the counters zero again, so calls issued one after
- *                    another on a stream may share it (concurrent calls on
- *                    different streams need separate workspaces).  When
- *                    the size function returns 0 no split is used and
+ *                    bytes, 256-byte aligned: one arrival counter per output
+ *                    tile in the first wsvd_append_counter_bytes(nb, nh, r)
+ *                    bytes, then fp32 split-E partial tiles.  The counter
+ *                    bytes must be zero when a call starts and every call
+ *                    leaves them zero (the same rule, and the same silent
+ *                    failure when it is broken, as the decode workspace's
+ *                    counters), so calls issued one after another on a
+ *                    stream may share a workspace zero-filled once as long
+ *                    as the counter area does not grow; concurrent calls on
+ *                    different streams need separate workspaces.  When the
+ *                    size function returns 0 no split is used and
  *                    workspace may be NULL.
  */
 int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap,
@@ -308,7 +325,7 @@ int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap,
  *
  *   K, V, kv_dt   [nb, nh, L_cap, H] BF16 (H in {64, 128}); L_cap * H below 2^30
  *   workspace     wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits)
- *                 bytes, counter area zero before first use (as above)
+ *                 bytes, same layout and zero-counter rule as above
  *   other arguments as for wsvd_decode_attn.
  */
 int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap,
@@ -328,17 +345,23 @@ int wsvd_decode_num_splits(int nb, int nh, int L_cap, int n_splits);
 /* Workspace bytes wsvd_decode_attn needs (0 on invalid sizes).  Pure host. */
 size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_splits);
 
-/* Byte offset of lse_part inside the decode workspace.  Pure host. */
-size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits);
+/* Bytes of the decode workspace's merge-counter area (offset 0): nb*nh
+ * uint32 rounded up to 256 (0 on invalid sizes).  Pure host. */
+size_t wsvd_decode_counter_bytes(int nb, int nh);
 
-/* Byte offset of the merge counters (nb*nh uint32) inside the decode
- * workspace.  Pure host. */
-size_t wsvd_decode_counter_offset(int nb, int nh, int H, int L_cap, int n_splits);
+/* Byte offsets of o_part and lse_part inside the decode workspace (0 on
+ * invalid sizes).  Pure host. */
+size_t wsvd_decode_opart_offset(int nb, int nh, int H, int L_cap, int n_splits);
+size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits);
 
 /* Workspace bytes wsvd_append_latent needs: 0 on invalid sizes, and 0 when
  * the sizes need no E split (then the workspace argument may be NULL).
  * Pure host. */
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r);
+
+/* Bytes of the append workspace's arrival-counter area (offset 0, one
+ * uint32 per output tile, rounded up to 256).  Pure host. */
+size_t wsvd_append_counter_bytes(int nb, int nh, int r);
 
 /*
  * Offline per-head factorisation (Arabic page section 2a, German page

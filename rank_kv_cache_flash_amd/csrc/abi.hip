@@ -76,35 +76,63 @@ int launch_with_merge(wsvd::DecodeArgs a, int H, Launch&& split, hipStream_t str
 
 }  // namespace
 
+extern "C" size_t wsvd_decode_counter_bytes(int nb, int nh);
+extern "C" size_t wsvd_decode_opart_offset(int nb, int nh, int H, int L_cap, int n_splits);
+extern "C" size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits);
+
+namespace {
+
+// Workspace layout: merge counters at byte 0 (nb * nh uint32, so their place
+// does not depend on the split count), then o_part, then lse_part, each
+// region 256-byte aligned.
+void set_decode_workspace(wsvd::DecodeArgs& a, void* workspace, int nb, int nh, int H, int L_cap, int n_splits) {
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<unsigned*>(ws);
+    a.o_part = reinterpret_cast<float*>(ws + wsvd_decode_opart_offset(nb, nh, H, L_cap, n_splits));
+    a.lse_part = reinterpret_cast<float*>(ws + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
+}
+
+}  // namespace
+
 extern "C" {
 
 int wsvd_decode_num_splits(int nb, int nh, int L_cap, int n_splits) {
     return resolve_splits(nb, nh, L_cap, n_splits);
 }
 
+size_t wsvd_decode_counter_bytes(int nb, int nh) {
+    if (nb <= 0 || nh <= 0) return 0;
+    return round_up((size_t)nb * nh * sizeof(unsigned), 256);
+}
+
+size_t wsvd_decode_opart_offset(int nb, int nh, int H, int L_cap, int n_splits) {
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0 || H <= 0) return 0;
+    return wsvd_decode_counter_bytes(nb, nh);
+}
+
 size_t wsvd_decode_lse_offset(int nb, int nh, int H, int L_cap, int n_splits) {
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0 || H <= 0) return 0;
-    return round_up(opart_bytes(nb, nh, H, S), 256);
-}
-
-size_t wsvd_decode_counter_offset(int nb, int nh, int H, int L_cap, int n_splits) {
-    const int S = resolve_splits(nb, nh, L_cap, n_splits);
-    if (S <= 0 || H <= 0) return 0;
-    return round_up(opart_bytes(nb, nh, H, S), 256) + round_up((size_t)nb * nh * S * sizeof(float), 256);
+    return wsvd_decode_counter_bytes(nb, nh) + round_up(opart_bytes(nb, nh, H, S), 256);
 }
 
 size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_splits) {
-    const size_t off = wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits);
-    if (off == 0) return 0;
-    return off + round_up((size_t)nb * nh * sizeof(unsigned), 256);
+    const int S = resolve_splits(nb, nh, L_cap, n_splits);
+    if (S <= 0 || H <= 0) return 0;
+    return wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits) + round_up((size_t)nb * nh * S * sizeof(float), 256);
+}
+
+size_t wsvd_append_counter_bytes(int nb, int nh, int r) {
+    if (nb <= 0 || nh <= 0 || r <= 0) return 0;
+    return round_up((size_t)wsvd::append_num_tiles(nb, nh, r) * sizeof(unsigned), 256);
 }
 
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r) {
     if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0) return 0;
     const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
     if (part == 0) return 0;
-    return round_up(part, 256) + round_up((size_t)wsvd::append_num_tiles(nb, nh, r) * sizeof(unsigned), 256);
+    return wsvd_append_counter_bytes(nb, nh, r) + round_up(part, 256);
 }
 
 const char* wsvd_status_string(int st) {
@@ -123,10 +151,12 @@ const char* wsvd_status_string(int st) {
 
 const char* wsvd_version(void) { return "wsvd 0.1 gfx950"; }
 
-int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, const void* q, wsvd_dtype q_dt,
-                     const void* C_K, const void* C_V, wsvd_dtype C_dt, const uint16_t* s_K, const uint16_t* s_V,
-                     const void* B_K, const void* B_V, wsvd_dtype B_dt, float softmax_scale, int n_splits,
-                     void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt, hipStream_t stream) {
+// Host checks of wsvd_decode_attn except the workspace; on success fills
+// everything in `a` but the workspace pointers.
+static int check_decode(int nb, int nh, int H, int r, int L_cap, const int32_t* L, const void* q, wsvd_dtype q_dt,
+                        const void* C_K, const void* C_V, wsvd_dtype C_dt, const uint16_t* s_K, const uint16_t* s_V,
+                        const void* B_K, const void* B_V, wsvd_dtype B_dt, float softmax_scale, int n_splits,
+                        void* out, wsvd_dtype out_dt, wsvd::DecodeArgs& a) {
     if (nb <= 0 || nh <= 0 || H <= 0 || r <= 0 || L_cap <= 0 || n_splits < 0 || r > H) return WSVD_ERR_SHAPE;
     if ((long long)nb * nh * L_cap * r > (1ll << 46)) return WSVD_ERR_SHAPE;
     if (!L || !q || !C_K || !C_V || !B_K || !B_V) return WSVD_ERR_NULL;
@@ -142,10 +172,8 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, 
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0) return WSVD_ERR_SHAPE;
     if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
-    const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
-    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
 
-    wsvd::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
     a.nb = nb;
     a.nh = nh;
     a.L_cap = L_cap;
@@ -162,12 +190,22 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, 
     a.B_dt = B_dt;
     const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
     a.scale_log2 = sigma * wsvd::kLog2e;
-    a.o_part = static_cast<float*>(workspace);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
-    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                             wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits));
     a.out = out;
     a.out_dt = out ? (int)out_dt : 0;
+    return WSVD_OK;
+}
+
+int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, const void* q, wsvd_dtype q_dt,
+                     const void* C_K, const void* C_V, wsvd_dtype C_dt, const uint16_t* s_K, const uint16_t* s_V,
+                     const void* B_K, const void* B_V, wsvd_dtype B_dt, float softmax_scale, int n_splits,
+                     void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt, hipStream_t stream) {
+    wsvd::DecodeArgs a;
+    const int st = check_decode(nb, nh, H, r, L_cap, L, q, q_dt, C_K, C_V, C_dt, s_K, s_V, B_K, B_V, B_dt,
+                                softmax_scale, n_splits, out, out_dt, a);
+    if (st != WSVD_OK) return st;
+    const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
+    set_decode_workspace(a, workspace, nb, nh, H, L_cap, n_splits);
 
     // With out and S > 1: on a grid that is resident in about two rounds the
     // last split of each head merges (one launch); on larger grids every
@@ -210,10 +248,7 @@ int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap, const int32_t* L, c
     a.B_dt = WSVD_BF16;
     const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
     a.scale_log2 = sigma * wsvd::kLog2e;
-    a.o_part = static_cast<float*>(workspace);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
-    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                             wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits));
+    set_decode_workspace(a, workspace, nb, nh, H, L_cap, n_splits);
     a.out = out;
     a.out_dt = out ? (int)out_dt : 0;
     return launch_with_merge(
@@ -265,10 +300,7 @@ int wsvd_decode_attn_rope(int nb, int nh, int H, int r, int L_cap, const int32_t
     a.B_dt = B_dt;
     const float sigma = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)H);
     a.scale_log2 = sigma * wsvd::kLog2e;
-    a.o_part = static_cast<float*>(workspace);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits));
-    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                             wsvd_decode_counter_offset(nb, nh, H, L_cap, n_splits));
+    set_decode_workspace(a, workspace, nb, nh, H, L_cap, n_splits);
     a.out = out;
     a.out_dt = out ? (int)out_dt : 0;
     return launch_with_merge(
@@ -351,10 +383,12 @@ static wsvd::AppendArgs append_args(int nb, int E, int nh, int r, int L_cap, con
     a.s_K = s_K;
     a.s_V = s_V;
     a.KS = wsvd::append_num_esplits(nb, E, nh, r);
+    // Counters at byte 0 (one per output tile), then the partial tiles.
     const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
-    const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
-    a.part = need > 0 ? static_cast<float*>(workspace) : nullptr;
-    a.counters = need > 0 ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + round_up(part, 256)) : nullptr;
+    a.counters = need > 0 ? static_cast<unsigned*>(workspace) : nullptr;
+    a.part = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                 wsvd_append_counter_bytes(nb, nh, r))
+                      : nullptr;
     return a;
 }
 

@@ -200,6 +200,52 @@ def make_ragged_step_inputs(nb, nh, H, r, E, L_lo, L_hi, L_cap, *, seed, q_gain=
     return inp
 
 
+def add_score_shift(inp: DecodeInputs, shift: float = 1000.0) -> DecodeInputs:
+    """Rebuild a step's inputs so that every attention score (default scale
+    1/sqrt(H)) carries one common offset of about `shift`.
+
+    The last latent column holds the same value c for every token, the
+    matching row of B_K maps it onto the first component of q alone, and that
+    component is 1:
+
+      * q[b, h, 0] = 1;
+      * C_K[..., r-1] = c: 1.0 for f32 / bf16 caches; for an int8 cache code
+        127 with every row's fp16 scale set to s0 = fp16(1/127) (so c = 127 s0
+        and every row dequantises with the same scale);
+      * B_K[h, r-1, :] = (a, 0, ..., 0) with a = shift sqrt(H) / c rounded to
+        the factor dtype.
+
+    The offset sigma c a q0 is exactly the same for every token of a head, so
+    attention is unchanged by it in exact arithmetic; its value is returned
+    in meta["score_shift"] and the input with a = 0 in meta["unshifted"]
+    (same tensors otherwise).  The caches keep rows past L[b] as they were.
+    Returns a new DecodeInputs; `inp` is not modified."""
+    import copy
+    out = copy.deepcopy(inp)
+    nb, nh, H = out.q.shape
+    r = out.r
+    one = {"f32": np.float32(1.0), "bf16": np.uint16(0x3F80), "f16": np.float16(1.0)}
+    out.q[:, :, 0] = one[out.q_dt]
+    if out.C_dt == "i8":
+        s0 = np.float16(1.0 / 127.0)
+        c = 127.0 * float(s0)
+        out.s_K[...] = s0
+        out.C_K[..., r - 1] = 127
+    else:
+        c = 1.0
+        out.C_K[..., r - 1] = one[out.C_dt]
+    a32 = np.float32(shift * np.sqrt(H) / c)
+    a_store = _store(np.array([a32], np.float32), out.B_dt)[0]
+    out.B_K[:, r - 1, :] = 0
+    twin = copy.deepcopy(out)
+    out.B_K[:, r - 1, 0] = a_store
+    a_val = float(np.asarray([a_store]).view(np.float32)[0]) if out.B_dt == "f32" else (
+        float(np.float16(a_store)) if out.B_dt == "f16" else
+        float((np.uint32(a_store) << np.uint32(16)).view(np.float32)))
+    out.meta = dict(out.meta, score_shift=c * a_val / np.sqrt(H), unshifted=twin)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # W8A8 projection inputs
 # ---------------------------------------------------------------------------

@@ -152,6 +152,103 @@ def test_binding_refuses_cpu_tensors(L):
         wsvd.decode_attn(q, c, c, b, b, torch.zeros(1, dtype=torch.int32))
 
 
+# Shape and dtype checks run on tensor metadata before the device check, so
+# every refusal below is reached with CPU tensors and launches nothing.
+def _dec(nb=2, nh=4, H=64, r=16, Lc=256, dt=torch.bfloat16, cdt=torch.bfloat16):
+    return dict(q=torch.zeros(nb, nh, H, dtype=dt), C_K=torch.zeros(nb, nh, Lc, r, dtype=cdt),
+                C_V=torch.zeros(nb, nh, Lc, r, dtype=cdt), B_K=torch.zeros(nh, r, H, dtype=dt),
+                B_V=torch.zeros(nh, r, H, dtype=dt), L=torch.zeros(nb, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("change,msg", [
+    (dict(C_V=torch.zeros(2, 4, 255, 16, dtype=torch.bfloat16)), "C_V must have shape"),
+    (dict(C_V=torch.zeros(2, 4, 256, 16, dtype=torch.float32)), "C_V must be one of"),
+    (dict(B_K=torch.zeros(4, 32, 64, dtype=torch.bfloat16)), "B_K must have shape"),
+    (dict(B_V=torch.zeros(4, 16, 64, dtype=torch.float16)), "B_V must be one of"),
+    (dict(L=torch.zeros(2, dtype=torch.int64)), "L must be one of"),
+    (dict(L=torch.zeros(3, dtype=torch.int32)), "L must have shape"),
+    (dict(out=torch.zeros(2, 4, 32, dtype=torch.bfloat16)), "out must have shape"),
+    (dict(q=torch.zeros(2, 4, 64, dtype=torch.int8)), "q must be one of"),
+    (dict(s_K=torch.zeros(2, 4, 256, dtype=torch.float16)), "int8 caches only"),
+])
+def test_binding_refuses_bad_decode_shapes(L, change, msg):
+    a = _dec()
+    a.update(change)
+    out = a.pop("out", None)
+    s_K = a.pop("s_K", None)
+    with pytest.raises(ValueError, match=msg):
+        wsvd.decode_attn(a["q"], a["C_K"], a["C_V"], a["B_K"], a["B_V"], a["L"], out=out, s_K=s_K)
+    with pytest.raises(ValueError, match=msg):
+        wsvd.PreparedDecode(a["q"], a["C_K"], a["C_V"], a["B_K"], a["B_V"], a["L"], out=out, s_K=s_K,
+                            workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_binding_int8_needs_scales_of_the_cache_shape(L):
+    a = _dec(cdt=torch.int8)
+    with pytest.raises(ValueError, match="s_K is required"):
+        wsvd.decode_attn(**a)
+    with pytest.raises(ValueError, match="s_V must have shape"):
+        wsvd.decode_attn(**a, s_K=torch.zeros(2, 4, 256, dtype=torch.float16),
+                         s_V=torch.zeros(2, 4, 128, dtype=torch.float16))
+
+
+def test_binding_refuses_bad_rope_dense_combine_shapes(L):
+    a = _dec()
+    c = torch.zeros(256, 32)
+    with pytest.raises(ValueError, match="rope_sin must have shape"):
+        wsvd.decode_attn_rope(a["q"], a["C_K"], a["C_V"], a["B_K"], a["B_V"], a["L"], c, torch.zeros(256, 16))
+    with pytest.raises(ValueError, match="C_K must be one of"):
+        wsvd.decode_attn_rope(a["q"], a["C_K"].float(), a["C_V"].float(), a["B_K"], a["B_V"], a["L"], c, c)
+    K = torch.zeros(2, 4, 256, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="V must have shape"):
+        wsvd.dense_decode_attn(a["q"], K, K[:, :, :200], a["L"])
+    with pytest.raises(ValueError, match="lse_part must have shape"):
+        wsvd.combine_splits(torch.zeros(2, 4, 3, 64), torch.zeros(2, 4, 2))
+
+
+def test_binding_refuses_bad_append_shapes(L):
+    bf = torch.bfloat16
+    x = torch.zeros(3, 512, dtype=bf)
+    A = torch.zeros(512, 4 * 32, dtype=bf)
+    C = torch.zeros(3, 4, 64, 32, dtype=bf)
+    pos = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="A_V must have shape"):
+        wsvd.append_latent(x, A, A[:, :64], pos, C, C)
+    with pytest.raises(ValueError, match="pos must have shape"):
+        wsvd.append_latent(x, A, A, pos[:2], C, C)
+    with pytest.raises(ValueError, match="C_K must hold 3 sequences"):
+        wsvd.append_latent(x, A, A, pos, C[:2], C[:2])
+    with pytest.raises(ValueError, match="x must be one of"):
+        wsvd.append_latent(x.float(), A, A, pos, C, C)
+    xq = torch.zeros(3, 512, dtype=torch.int8)
+    Aq = torch.zeros(128, 512, dtype=torch.int8)
+    sA = torch.zeros(128)
+    with pytest.raises(ValueError, match="AqT_V must have shape"):
+        wsvd.append_latent_w8a8(xq, torch.zeros(3), Aq, sA, Aq[:64], sA, pos, C, C)
+    with pytest.raises(ValueError, match="sx must have shape"):
+        wsvd.append_latent_w8a8(xq, torch.zeros(4), Aq, sA, Aq, sA, pos, C, C)
+
+
+def test_binding_zero_counter_rule(L):
+    """A workspace this module zero-filled remembers how much of it is still
+    known to be zero; a call whose counter area reaches past that is refused
+    before anything is launched."""
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    wsvd._zero_filled(ws)
+    wsvd._claim_counters(ws, 256, "first call")        # a small batch: partials from byte 256 on
+    assert ws._wsvd_zero_bytes == 256
+    wsvd._claim_counters(ws, 256, "same size")
+    with pytest.raises(ValueError, match="must be zero"):
+        wsvd._claim_counters(ws, 512, "larger batch")
+    ws2 = wsvd._zero_filled(torch.zeros(4096, dtype=torch.uint8))
+    wsvd._claim_counters(ws2, 512, "partials only", needs_zero=False)   # writes past byte 512, merges nothing
+    wsvd._claim_counters(ws2, 512, "then with an output")
+    with pytest.raises(ValueError, match="must be zero"):
+        wsvd._claim_counters(ws2, 768, "larger batch")
+    plain = torch.zeros(16, dtype=torch.uint8)          # not from this module: the caller's responsibility
+    wsvd._claim_counters(plain, 1 << 20, "unmarked")
+
+
 def dense(L, **kw):
     a = dict(nb=2, nh=4, H=128, L_cap=256, Lp=P, q=P, q_dt=BF16, K=P, V=P, kv_dt=BF16, S=0, ws=P, ws_bytes=WS,
              out=P, out_dt=BF16)
@@ -311,3 +408,4 @@ def test_shared_workspace_size(L):
 ])
 def test_shared_rejects(L, kw, want):
     assert shared(L, **kw) == want
+

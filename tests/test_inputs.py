@@ -84,3 +84,35 @@ def test_byte_model_matches_hand_totals():
     L = c5.draw_L()
     assert c5.decode_bytes(L) == 6_144 * int(L.sum()) + 786_432 + 1_048_576
     assert np.all((L >= 1024) & (L <= 8192))
+
+
+@pytest.mark.parametrize("C_dt,act", [("f32", "f32"), ("bf16", "bf16"), ("i8", "bf16")])
+def test_score_shift_construction(C_dt, act):
+    """add_score_shift: every score of a head moves by one constant of about
+    1000 (scores written out here as sigma * sum_i c_i (B_K q)_i from the
+    stored values, independently of the oracle), and the oracle's output is
+    unchanged by it (softmax is shift invariant; an oracle without its max
+    subtraction would overflow at these scores)."""
+    import oracle as O
+    L = np.array([300, 1, 0, 129], np.int32)
+    inp = I.make_decode_inputs(4, 3, 128, 32, L, 300, seed=11, act_dt=act, C_dt=C_dt, q_gain=4.0 * 128)
+    sh = I.add_score_shift(inp)
+    tw = sh.meta["unshifted"]
+    assert 990.0 < sh.meta["score_shift"] < 1010.0
+    assert not np.array_equal(inp.q, sh.q)            # the input was copied, not changed in place
+
+    def scores(x, b, h):
+        n = int(x.L[b])
+        c = O.upcast(x.C_K[b, h, :n], x.C_dt)
+        if x.C_dt == "i8":
+            c = c * O.upcast(x.s_K[b, h, :n], "f16")[:, None]
+        qp = O.upcast(x.B_K[h], x.B_dt) @ O.upcast(x.q[b, h], x.q_dt)      # [r]
+        return np.array([sum(c[t, i] * qp[i] for i in range(x.r)) for t in range(n)]) / np.sqrt(128)
+
+    for b, h in ((0, 0), (0, 2), (1, 1), (3, 2)):
+        d = scores(sh, b, h) - scores(tw, b, h)
+        np.testing.assert_allclose(d, sh.meta["score_shift"], rtol=1e-12)
+    a, t = O.decode_attn(sh), O.decode_attn(tw)
+    assert np.all(np.isfinite(a))
+    assert np.max(np.abs(a - t)) <= 1e-9 * np.max(np.abs(t))
+    assert not a[2].any()                               # L = 0 still gives a zero row
