@@ -150,6 +150,38 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap,
                      hipStream_t stream);
 
 /*
+ * wsvd_decode_attn_noalloc -- wsvd_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and the call
+ * allocates nothing.  Arguments, results and kernels are those of
+ * wsvd_decode_attn with an output (out must not be NULL: the partials stay
+ * in the library's scratch).
+ *
+ * Scratch: one static device array per GPU, held from the library's load
+ * until the process ends: merge counters for up to 65536 (b, h) pairs in a
+ * region of their own (256 KiB, zero at start, and every call leaves them
+ * zero), then 16 MiB for the split partials, laid out as in the decode
+ * workspace.  Calls whose nb * nh exceeds 65536, or whose partials
+ * (wsvd_decode_workspace_bytes(...) - wsvd_decode_counter_bytes(nb, nh))
+ * exceed 16 MiB, return WSVD_ERR_WORKSPACE with nothing launched.  The
+ * first call on a device looks the array up and zero-fills the counter
+ * region on `stream`.  The scratch of the current device is used; `stream`
+ * must belong to it.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or several host
+ * threads without ordering) race on it and give wrong results.  Calls
+ * ordered on one stream are safe.
+ */
+int wsvd_decode_attn_noalloc(int nb, int nh, int H, int r, int L_cap,
+                             const int32_t* L,
+                             const void* q, wsvd_dtype q_dt,
+                             const void* C_K, const void* C_V, wsvd_dtype C_dt,
+                             const uint16_t* s_K, const uint16_t* s_V,
+                             const void* B_K, const void* B_V, wsvd_dtype B_dt,
+                             float softmax_scale, int n_splits,
+                             void* out, wsvd_dtype out_dt,
+                             hipStream_t stream);
+
+/*
  * wsvd_combine_splits -- merge per-split partials into the attention output.
  *
  * The Flash-Decoding pass named on the German page section 2D (and the

@@ -7,8 +7,21 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
+
+// Scratch of wsvd_decode_attn_noalloc, one copy per GPU for the life of the
+// process: merge counters for up to kNoallocPairs (b, h) pairs in a region of
+// their own (every call leaves them zero, so they never need clearing
+// again), then the split partials (o_part, lse_part).  Host code never uses
+// the name of this array as an address: each device's address comes from
+// hipGetSymbolAddress (see noalloc_scratch below).
+constexpr size_t kNoallocPairs = 65536;
+constexpr size_t kNoallocCounterBytes = kNoallocPairs * sizeof(unsigned);   // 256 KiB
+constexpr size_t kNoallocPartialBytes = size_t(16) << 20;                   // 16 MiB
+static __device__ __align__(256) unsigned char scratch[kNoallocCounterBytes + kNoallocPartialBytes];
 
 namespace {
 
@@ -72,6 +85,36 @@ int launch_with_merge(wsvd::DecodeArgs a, int H, Launch&& split, hipStream_t str
     return wsvd::launch_combine(a.nb, a.nh, H, a.S, a.o_part, a.lse_part, out, a.out_dt, stream) == hipSuccess
                ? WSVD_OK
                : WSVD_ERR_HIP;
+}
+
+// Per-device address of `scratch`, looked up once per device with that
+// device current; the first lookup also zero-fills the counter region on the
+// caller's stream (device globals start zeroed, so this only makes the
+// starting state explicit).
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+hipError_t noalloc_scratch(hipStream_t stream, char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&] {
+        void* p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess)
+            slot.err = wsvd::launch_fill_zero_u32(static_cast<unsigned*>(p), kNoallocPairs, stream);
+        if (slot.err == hipSuccess) slot.ptr = p;
+    });
+    if (slot.err != hipSuccess) return slot.err;
+    *out = static_cast<char*>(slot.ptr);
+    return hipSuccess;
 }
 
 }  // namespace
@@ -211,6 +254,31 @@ int wsvd_decode_attn(int nb, int nh, int H, int r, int L_cap, const int32_t* L, 
     // last split of each head merges (one launch); on larger grids every
     // block would otherwise hold its slot through the store-and-arrive round
     // trip, so the splits write partials only and the merge kernel follows.
+    return launch_with_merge(
+        a, H, [&](const wsvd::DecodeArgs& x) { return wsvd::launch_decode_split(x, H, r, C_dt, stream); }, stream);
+}
+
+int wsvd_decode_attn_noalloc(int nb, int nh, int H, int r, int L_cap, const int32_t* L, const void* q,
+                             wsvd_dtype q_dt, const void* C_K, const void* C_V, wsvd_dtype C_dt, const uint16_t* s_K,
+                             const uint16_t* s_V, const void* B_K, const void* B_V, wsvd_dtype B_dt,
+                             float softmax_scale, int n_splits, void* out, wsvd_dtype out_dt, hipStream_t stream) {
+    if (!out) return WSVD_ERR_NULL;  // the partials stay in the library's scratch: only out is a result
+    wsvd::DecodeArgs a;
+    const int st = check_decode(nb, nh, H, r, L_cap, L, q, q_dt, C_K, C_V, C_dt, s_K, s_V, B_K, B_V, B_dt,
+                                softmax_scale, n_splits, out, out_dt, a);
+    if (st != WSVD_OK) return st;
+    // The partial regions laid out as in a caller workspace, after the fixed
+    // counter region; sizes beyond the scratch are refused.
+    const size_t part = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits) - wsvd_decode_counter_bytes(nb, nh);
+    if ((size_t)nb * nh > kNoallocPairs || part > kNoallocPartialBytes) return WSVD_ERR_WORKSPACE;
+    char* base = nullptr;
+    if (noalloc_scratch(stream, &base) != hipSuccess) return WSVD_ERR_HIP;
+    const size_t ctr = wsvd_decode_counter_bytes(nb, nh);
+    a.counters = reinterpret_cast<unsigned*>(base);
+    a.o_part = reinterpret_cast<float*>(base + kNoallocCounterBytes +
+                                        (wsvd_decode_opart_offset(nb, nh, H, L_cap, n_splits) - ctr));
+    a.lse_part = reinterpret_cast<float*>(base + kNoallocCounterBytes +
+                                          (wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits) - ctr));
     return launch_with_merge(
         a, H, [&](const wsvd::DecodeArgs& x) { return wsvd::launch_decode_split(x, H, r, C_dt, stream); }, stream);
 }

@@ -61,6 +61,19 @@ __global__ __launch_bounds__(256) void combine_kernel(int nbh, int H, int S, con
     store_elem_wt(out, out_dt, (size_t)row * H + t, v);
 }
 
+// Zero n uint32 words with vector stores (a kernel rather than a memset, so
+// it can sit in a captured graph like the calls around it).
+__global__ __launch_bounds__(256) void fill_zero_u32_kernel(unsigned* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_fill_zero_u32(unsigned* p, size_t n, hipStream_t st) {
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned)(blocks < 1024 ? (blocks ? blocks : 1) : 1024)),
+                       dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, const float* lse_part, void* out,
                           int out_dt, hipStream_t st) {
     const int nbh = nb * nh;

@@ -44,6 +44,8 @@ hipError_t launch_dense_split(const DecodeArgs& a, int H, hipStream_t st);
 
 hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, const float* lse_part,
                           void* out, int out_dt, hipStream_t st);
+// p[0 .. n) = 0 (uint32 words), one small launch.
+hipError_t launch_fill_zero_u32(unsigned* p, size_t n, hipStream_t st);
 
 struct AppendArgs {
     int nb, E, nh, r, L_cap;

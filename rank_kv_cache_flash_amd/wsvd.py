@@ -39,6 +39,9 @@ def lib() -> ctypes.CDLL:
     L.wsvd_decode_attn.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32,
                                    f32, i32, vp, sz, vp, i32, vp]
     L.wsvd_decode_attn.restype = i32
+    L.wsvd_decode_attn_noalloc.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32,
+                                           f32, i32, vp, i32, vp]
+    L.wsvd_decode_attn_noalloc.restype = i32
     L.wsvd_dense_decode_attn.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, f32, i32, vp, sz, vp, i32, vp]
     L.wsvd_dense_decode_attn.restype = i32
     L.wsvd_combine_splits.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
@@ -276,6 +279,29 @@ def decode_attn(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=N
         _ptr(out), _DT[out.dtype] if out is not None else 0, _stream(stream))
     _check(st, "wsvd_decode_attn")
     return (out, *_partial_views(workspace, nb, nh, H, L_cap, n_splits, S))
+
+
+def decode_attn_noalloc(q, C_K, C_V, B_K, B_V, L, *, s_K=None, s_V=None, softmax_scale=None, n_splits=None,
+                        out=None, out_dtype=None, stream=None):
+    """wsvd_decode_attn_noalloc: decode_attn with no workspace (the library's
+    per-GPU static scratch holds the partials); returns out.  Calls that
+    overlap on one GPU race on that scratch."""
+    nb, nh, H, L_cap, r = _check_decode_args(q, C_K, C_V, B_K, B_V, L, s_K, s_V, out)
+    for t, n in ((q, "q"), (C_K, "C_K"), (C_V, "C_V"), (B_K, "B_K"), (B_V, "B_V"), (L, "L"),
+                 (s_K, "s_K"), (s_V, "s_V"), (out, "out")):
+        _dev(t, n)
+    if out is None:
+        out = torch.empty((nb, nh, H), dtype=out_dtype or q.dtype, device=q.device)
+    if s_K is not None and s_K.dtype == torch.float16:
+        s_K = s_K.view(torch.int16)
+    if s_V is not None and s_V.dtype == torch.float16:
+        s_V = s_V.view(torch.int16)
+    st = lib().wsvd_decode_attn_noalloc(
+        nb, nh, H, r, L_cap, _ptr(L), _ptr(q), _DT[q.dtype], _ptr(C_K), _ptr(C_V), _DT[C_K.dtype],
+        _ptr(s_K), _ptr(s_V), _ptr(B_K), _ptr(B_V), _DT[B_K.dtype], float(softmax_scale or 0.0), int(n_splits or 0),
+        _ptr(out), _DT[out.dtype], _stream(stream))
+    _check(st, "wsvd_decode_attn_noalloc")
+    return out
 
 
 def _partial_views(workspace, nb, nh, H, L_cap, n_splits, S):

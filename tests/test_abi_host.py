@@ -409,3 +409,25 @@ def test_shared_workspace_size(L):
 def test_shared_rejects(L, kw, want):
     assert shared(L, **kw) == want
 
+
+def noalloc(L, **kw):
+    a = dict(nb=1, nh=32, H=128, r=32, L_cap=1088, Lp=P, q=P, q_dt=BF16, C_K=P, C_V=P, C_dt=BF16, s_K=None,
+             s_V=None, B_K=P, B_V=P, B_dt=BF16, scale=0.0, S=0, out=P, out_dt=BF16)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return L.wsvd_decode_attn_noalloc(a["nb"], a["nh"], a["H"], a["r"], a["L_cap"], v(a["Lp"]), v(a["q"]),
+                                      a["q_dt"], v(a["C_K"]), v(a["C_V"]), a["C_dt"], v(a["s_K"]), v(a["s_V"]),
+                                      v(a["B_K"]), v(a["B_V"]), a["B_dt"], a["scale"], a["S"], v(a["out"]),
+                                      a["out_dt"], None)
+
+
+# Every case is refused by the host checks, all of which run before the
+# scratch is looked up (the lookup is the first HIP call).
+@pytest.mark.parametrize("kw,want", [
+    (dict(out=None), ENULL), (dict(q=None), ENULL), (dict(nb=0), ESHAPE), (dict(r=160), ESHAPE),
+    (dict(H=96, r=32), EUNSUP), (dict(C_dt=F16), EDTYPE), (dict(q=P + 4), EALIGN),
+    (dict(nb=65537, nh=1, L_cap=16), EWS),                      # more (b, h) pairs than the counter region holds
+    (dict(L_cap=1 << 20, S=1100), EWS),                         # 32 x 1100 x 128 fp32 partials > 16 MiB
+])
+def test_decode_noalloc_rejects(L, kw, want):
+    assert noalloc(L, **kw) == want
