@@ -1,22 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the WSVD low-rank decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--also 3,4,5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--also 2,3,4]
 
-A step is one pass of the whole hot path over one batch: (append of the new
-token's latents when the workload has one, then) the split decode and the
-split merge.  Inputs are resident in HBM before timing starts.  Steps are
-captured once into a HIP graph (rotating through enough copies of the
-inputs that every step reads cold HBM) and the graph is replayed; the K
-timed steps are bracketed by device synchronisation and timed with events
-on the replay stream.
+A step is one pass of the whole hot path over one batch: the append of the
+new token's latents (x . A_Kh, x . A_Vh into row L[b] - 1 of every head's
+caches) when the workload has one, then the split decode and the split
+merge.  The headline workload is the full step (workload 5, the largest).
+Inputs are resident in HBM before timing starts.
+
+Timing: the steps are captured once into a HIP graph holding K steps (at
+least one per input copy, and enough copies that one replay reads >= 1 GiB
+of distinct inputs, so every step reads cold HBM rather than the 256 MB
+Infinity Cache).  After W eager warm-up steps and one untimed replay, each
+timed region is one or more back-to-back replays (>= 1 ms) between events on
+the replay stream, bracketed by device synchronisation; the median over five
+regions is reported with every region's figure.
 
 Prints ONE JSON line.  `value` is achieved GB/s = algorithmic bytes per step
 / time per step (higher is better); `ms_per_step` gives the time.  The
-`roofline` object covers the dominant kernel (the split decode), timed live
-in its own graph of K back-to-back launches; `cpu_baseline` is the fp64
-oracle timed on the host on a bounded sample; `per_config` repeats the
-measurement on the other workloads with fewer steps.
+`roofline` object covers the dominant kernel (the split decode), timed the
+same way in its own graph of back-to-back launches; `cpu_baseline` is the
+fp64 oracle timed on the host on a bounded sample; `per_config` repeats the
+whole measurement (with its own roofline and oracle baseline) on the other
+workloads.
 """
 from __future__ import annotations
 
@@ -111,14 +118,26 @@ class Workload:
         self.dec_only[i % self.copies]()
 
 
-def graph_time(fn, n, warmup_eager, repeats=1):
-    """Capture n calls of fn(i) in one graph; replay; return seconds per call
-    for each timed replay (first replay is untimed)."""
+MIN_REGION_S = 1e-3      # every timed region lasts at least this long
+REGIONS = 5              # timed regions per measurement; the median is reported
+
+
+def graph_timing(fn, steps, warmup, copies=1, min_region_s=MIN_REGION_S, regions=REGIONS):
+    """Seconds per call of fn(i), from a HIP graph replayed on the current stream.
+
+    The graph holds n calls, n = `steps` rounded up to a multiple of
+    `copies`, so one replay touches every input copy (callers size `copies`
+    so that is >= 1 GiB) whatever `steps` is.  After `warmup` eager calls and
+    one untimed replay, each timed region is k back-to-back replays between
+    two events on the replay stream (k chosen so a region lasts >=
+    min_region_s), bracketed by device synchronisation; the median over
+    `regions` regions is returned with every region's figure."""
     import torch
+    n = max(1, -(-max(steps, copies) // copies) * copies)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in range(warmup_eager):
+        for i in range(warmup):
             fn(i)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
@@ -128,18 +147,28 @@ def graph_time(fn, n, warmup_eager, repeats=1):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    out = []
-    for _ in range(repeats):
+
+    def region(k):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        g.replay()
+        for _ in range(k):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) * 1e-3 / n)
+        return e0.elapsed_time(e1) * 1e-3
+
+    k = max(1, math.ceil(min_region_s / max(region(1), 1e-9)))
+    per = [region(k) / (k * n) for _ in range(regions)]
     del g
-    return out
+    return {"s_per_call": statistics.median(per), "regions_s_per_call": per, "graph_calls": n,
+            "replays_per_region": k, "regions": regions}
+
+
+def graph_time(fn, steps, warmup, copies=1):
+    """Median seconds per call (graph_timing)."""
+    return graph_timing(fn, steps, warmup, copies)["s_per_call"]
 
 
 def eager_time(fn, n, warmup):
@@ -202,15 +231,15 @@ def append_variants(cfg, steps, warmup=10, seed=0):
     xq = torch.empty(nb, E, dtype=torch.int8, device="cuda")
     sx = torch.empty(nb, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    t_bf = graph_time(lambda i: bf_calls[i % ncopy](torch.cuda.current_stream()), steps, warmup)[0]
+    t_bf = graph_time(lambda i: bf_calls[i % ncopy](torch.cuda.current_stream()), steps, warmup, ncopy)
 
     def w8_step(i):
         AKq, sAK, AVq, sAV = w8_facs[i % ncopy]
         wsvd.w8a8_quantize_activations(x, xq=xq, sx=sx)
         wsvd.append_latent_w8a8(xq, sx, AKq, sAK, AVq, sAV, pos, C_K, C_V, workspace=ws)
 
-    t_w8 = graph_time(w8_step, steps, warmup)[0]
-    t_q = graph_time(lambda i: wsvd.w8a8_quantize_activations(x, xq=xq, sx=sx), steps, warmup)[0]
+    t_w8 = graph_time(w8_step, steps, warmup, ncopy)
+    t_q = graph_time(lambda i: wsvd.w8a8_quantize_activations(x, xq=xq, sx=sx), steps, warmup)
     b_bf = 2 * E * N * 2 + nb * E * 2 + nb * 2 * N * 2
     b_w8 = 2 * E * N + 2 * N * 4 + nb * E * (2 + 1) + nb * 4 + nb * 2 * N * 2
     del bf_calls, w8_facs
@@ -243,7 +272,7 @@ def rope_vs_folded(w, steps, warmup=10):
         ws = wsvd.decode_workspace(cfg.nb, cfg.nh, cfg.H, cfg.L_cap, 0)
         calls.append(wsvd.PreparedDecodeRope(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], c, s_,
                                              workspace=ws, out=out))
-    t = graph_time(lambda i: calls[i % len(calls)](), steps, warmup)[0]
+    t = graph_time(lambda i: calls[i % len(calls)](), steps, warmup, len(calls))
     nbytes = w.step_bytes + cfg.L_cap * cfg.H * 4
     del calls
     return {"us_per_step": round(t * 1e6, 3), "GB_per_s": round(nbytes / t / 1e9, 1),
@@ -311,19 +340,20 @@ def factorize_offline(E=4096, nh=32, H=128, ranks=(32, 64), iters=5, cpu=True, s
 # ---------------------------------------------------------------------------
 # dense Flash-Decoding baseline at the same shape (the pages' comparison)
 # ---------------------------------------------------------------------------
-def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
+def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0, L_cap=None):
     """Time the WSVD decode step and dense Flash-Decoding on equal shapes.
 
     Random GPU-side bf16 inputs (timing only; parity is covered by the
     tests), cold-HBM rotation for both, graph replay of `steps` steps.
-    L is an int or an int array [nb]; the cache capacity is max(L).
+    L is an int or an int array [nb]; the cache capacity is L_cap (default
+    max(L)).
     """
     import numpy as np
     import torch
     from rank_kv_cache_flash_amd import wsvd
 
     Ls = np.broadcast_to(np.asarray(L, dtype=np.int64), (nb,))
-    L_cap = int(Ls.max())
+    L_cap = int(Ls.max()) if L_cap is None else int(L_cap)
     g = torch.Generator(device="cuda").manual_seed(seed)
     bf = torch.bfloat16
 
@@ -331,7 +361,7 @@ def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
         return (torch.randn(*shape, generator=g, device="cuda") * scale).to(bf)
 
     def copies_for(nbytes):
-        return max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
+        return max(1, min(256, math.ceil(COLD_BYTES / nbytes)))
 
     wb = int(Ls.sum()) * nh * 2 * r * 2 + nh * 2 * r * H * 2 + nb * nh * H * 4
     db = int(Ls.sum()) * nh * 2 * H * 2 + nb * nh * H * 4
@@ -345,14 +375,14 @@ def dense_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
         CK, CV = rnd(nb, nh, L_cap, r, scale=r ** -0.5), rnd(nb, nh, L_cap, r, scale=r ** -0.5)
         BK, BV = rnd(nh, r, H, scale=H ** -0.5), rnd(nh, r, H, scale=H ** -0.5)
         w_calls.append(wsvd.PreparedDecode(q, CK, CV, BK, BV, Lt, workspace=ws, out=out))
-    t_w = graph_time(lambda i: w_calls[i % len(w_calls)](), steps, warmup)[0]
+    t_w = graph_time(lambda i: w_calls[i % len(w_calls)](), steps, warmup, len(w_calls))
     del w_calls
     torch.cuda.empty_cache()
     for _ in range(copies_for(db)):
         q = rnd(nb, nh, H, scale=H ** -0.5)
         K, V = rnd(nb, nh, L_cap, H, scale=H ** -0.5), rnd(nb, nh, L_cap, H, scale=H ** -0.5)
         d_calls.append(wsvd.PreparedDense(q, K, V, Lt, workspace=ws2, out=out))
-    t_d = graph_time(lambda i: d_calls[i % len(d_calls)](), steps, warmup)[0]
+    t_d = graph_time(lambda i: d_calls[i % len(d_calls)](), steps, warmup, len(d_calls))
     del d_calls
     torch.cuda.empty_cache()
     return {"nb": nb, "nh": nh, "H": H, "r": r, "L_sum": int(Ls.sum()), "L_cap": L_cap,
@@ -408,7 +438,7 @@ def shared_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
     sb_streamed = nh * latent + s_fact + 2 * nb * nh * H * 2
 
     def copies_for(nbytes):
-        return max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
+        return max(1, min(256, math.ceil(COLD_BYTES / nbytes)))
 
     ws = wsvd.decode_workspace(nb, nh, H, L_cap, 0)
     w_calls = []
@@ -419,11 +449,11 @@ def shared_vs_wsvd(nb, nh, H, r, L, steps, warmup=10, seed=0):
         BK = (torch.randn(nh, r, H, generator=g, device="cuda") * H ** -0.5).to(bf)
         BV = (torch.randn(nh, r, H, generator=g, device="cuda") * H ** -0.5).to(bf)
         w_calls.append(wsvd.PreparedDecode(q, CK, CV, BK, BV, Lt, workspace=ws, out=out))
-    t_w = graph_time(lambda i: w_calls[i % len(w_calls)](), steps, warmup)[0]
+    t_w = graph_time(lambda i: w_calls[i % len(w_calls)](), steps, warmup, len(w_calls))
     del w_calls
     torch.cuda.empty_cache()
     s_calls = _shared_calls(nb, nh, H, R, L_cap, Lt, g, copies_for(sb_unique), out)
-    t_s = graph_time(lambda i: s_calls[i % len(s_calls)](), steps, warmup)[0]
+    t_s = graph_time(lambda i: s_calls[i % len(s_calls)](), steps, warmup, len(s_calls))
     del s_calls
     torch.cuda.empty_cache()
     return {"nb": nb, "nh": nh, "H": H, "r": r, "R": R, "L": L_cap, "r_over_R": round(r / R, 5),
@@ -501,48 +531,74 @@ def cpu_baseline(w, gpu_out, budget_s=12.0):
 
 
 # ---------------------------------------------------------------------------
-def measure(cfg, steps, warmup, n_splits=None, repeats=3):
+def measure(cfg, steps, warmup, n_splits=None, cpu_budget=None, extras=True):
+    """One workload: the whole step (append when the workload has one, split
+    decode, merge), the dominant kernel alone for the roofline, a labelled
+    warm-cache figure, the oracle on the host, and (extras) the dense
+    Flash-Decoding and rotary-key comparisons on the same shapes."""
+    import torch
     w = Workload(cfg, n_splits=n_splits)
-    t_step = graph_time(w.step, steps, warmup, repeats=repeats)
-    t_dec = graph_time(w.decode_only, steps, warmup, repeats=repeats)
+    t_step = graph_timing(w.step, steps, warmup, w.copies)
+    t_dec = graph_timing(w.decode_only, steps, warmup, w.copies)
     # Warm: every step on input copy 0, so whatever fits stays in L2 / the
     # Infinity Cache (256 MB).  Reported beside the cold figure, labelled.
-    w.t_warm = graph_time(lambda i: w.step(0), steps, warmup)[0]
-    return w, t_step, t_dec
-
-
-def summary(cfg, w, t_step, t_dec):
-    ts = t_step[0]
-    td = statistics.median(t_dec)
-    return {
+    t_warm = graph_timing(lambda i: w.step(0), steps, warmup)
+    ts, td, tw = t_step["s_per_call"], t_dec["s_per_call"], t_warm["s_per_call"]
+    achieved = w.decode_kernel_bytes / td / 1e9
+    rec = {
         "workload": cfg.name,
         "shape": cfg.describe(),
         "us_per_step": round(ts * 1e6, 3),
-        "us_per_step_replays": [round(t * 1e6, 3) for t in t_step],
         "GB_per_s": round(w.step_bytes / ts / 1e9, 1),
         "pct_of_hbm_peak": round(100.0 * w.step_bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
         "step_bytes": int(w.step_bytes),
-        "decode_kernel_us": round(td * 1e6, 3),
-        "decode_kernel_GB_per_s": round(w.decode_kernel_bytes / td / 1e9, 1),
         "splits": w.S,
         "input_copies": w.copies,
-        "warm_cache": {"us_per_step": round(w.t_warm * 1e6, 3),
-                       "GB_per_s": round(w.step_bytes / w.t_warm / 1e9, 1),
-                       "note": "every step on one input copy (cache-resident where it fits); "
-                               "not an HBM figure"},
+        "timing": {"graph_calls": t_step["graph_calls"], "replays_per_region": t_step["replays_per_region"],
+                   "regions": t_step["regions"], "statistic": "median over regions",
+                   "regions_us_per_step": [round(t * 1e6, 3) for t in t_step["regions_s_per_call"]],
+                   "distinct_bytes_per_replay": int(w.step_bytes * min(t_step["graph_calls"], w.copies))},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(cfg.name, w.decode_kernel_bytes),
+                     "kernel": "decode_split_kernel", "alg_bytes_per_launch": int(w.decode_kernel_bytes),
+                     "avg_launch_us": round(td * 1e6, 3),
+                     "launch_regions_us": [round(t * 1e6, 3) for t in t_dec["regions_s_per_call"]]},
+        "warm_cache": {"us_per_step": round(tw * 1e6, 3), "GB_per_s": round(w.step_bytes / tw / 1e9, 1),
+                       "note": "every step on one input copy (cache-resident where it fits); not an HBM figure"},
     }
+    if cpu_budget:
+        torch.cuda.synchronize()
+        rec["cpu_baseline"], rec["parity_max_rel_err_vs_oracle"] = cpu_baseline(w, w.out, budget_s=cpu_budget)
+    if extras:
+        rope = rope_vs_folded(w, steps, min(warmup, 10))
+        if rope is not None:
+            rec["rotary_keys"] = rope
+    L = w.L.copy()
+    del w
+    torch.cuda.empty_cache()
+    if extras and cfg.C_dt == "bf16":
+        Lx = L if cfg.has_append else cfg.L
+        rec["vs_dense_flash_decoding"] = dense_vs_wsvd(cfg.nb, cfg.nh, cfg.H, cfg.r, Lx, steps, min(warmup, 10),
+                                                       L_cap=cfg.L_cap)
+        if cfg.has_append:
+            rec["vs_dense_flash_decoding"]["note"] = "decode only (no append) at the workload's ragged lengths"
+    if extras and cfg.has_append:
+        rec["append_alone"] = append_variants(cfg, max(steps, 100), min(warmup, 10))
+    return rec
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--also", default="3,4,5", help="other workloads measured into per_config ('' for none)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--also", default="2,3,4", help="other workloads measured into per_config ('' for none)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle seconds for the headline workload")
+    ap.add_argument("--cpu-budget-other", type=float, default=4.0, help="oracle seconds for each other workload")
     ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep",
                                        "factorize-loop", "shared-loop", "rope-loop", "append-loop"],
                     default="bench",
@@ -709,56 +765,25 @@ def main():
         return
 
     cfg = CONFIGS[args.config]
-    w, t_step, t_dec = measure(cfg, args.steps, args.warmup, n_splits=args.splits or None)
-    main_sum = summary(cfg, w, t_step, t_dec)
-    ts = t_step[0]
-    td = statistics.median(t_dec)
-
-    achieved = w.decode_kernel_bytes / td / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(cfg.name, w.decode_kernel_bytes),
-                "kernel": "decode_split_kernel", "alg_bytes_per_launch": int(w.decode_kernel_bytes),
-                "avg_launch_us": round(td * 1e6, 3)}
-
-    cpu = None
-    parity = None
-    if not args.no_cpu:
-        torch.cuda.synchronize()
-        cpu, parity = cpu_baseline(w, w.out, budget_s=args.cpu_budget)
-
-    rope_main = rope_vs_folded(w, args.steps, min(args.warmup, 10))
-
-    vs_dense = None
-    if not cfg.has_append and cfg.C_dt == "bf16":
-        vs_dense = dense_vs_wsvd(cfg.nb, cfg.nh, cfg.H, cfg.r, cfg.L, args.steps, min(args.warmup, 10))
+    main_rec = measure(cfg, args.steps, args.warmup, n_splits=args.splits or None,
+                       cpu_budget=None if args.no_cpu else args.cpu_budget)
 
     per = {}
     also = [int(x) for x in args.also.split(",") if x.strip()] if args.also else []
-    del w
-    torch.cuda.empty_cache()
     for cid in also:
         if cid == args.config:
             continue
         c = CONFIGS[cid]
-        k = max(10, min(args.steps, int(2e-2 / max(c.step_bytes() / 6e12, 1e-7))))
-        wc, tsc, tdc = measure(c, k, min(args.warmup, 10))
-        per[c.name] = summary(c, wc, tsc, tdc)
-        per[c.name]["steps"] = k
-        rope = rope_vs_folded(wc, k, min(args.warmup, 10))
-        if rope is not None:
-            per[c.name]["rotary_keys"] = rope
-        del wc
+        per[c.name] = measure(c, args.steps, min(args.warmup, 10),
+                              cpu_budget=None if args.no_cpu else args.cpu_budget_other)
+        per[c.name]["steps"] = args.steps
         torch.cuda.empty_cache()
-        if c.has_append:
-            per[c.name]["append_alone"] = append_variants(c, max(k, 100), min(args.warmup, 10))
 
     ablation = None
     if args.shared:
         ablation = {}
         for cid, (nb_, nh_, H_, r_, L_) in SHARED_SHAPES.items():
-            k = 200 if cid == 2 else 10
-            ablation[CONFIGS[cid].name] = shared_vs_wsvd(nb_, nh_, H_, r_, L_, k, min(args.warmup, 5))
+            ablation[CONFIGS[cid].name] = shared_vs_wsvd(nb_, nh_, H_, r_, L_, args.steps, min(args.warmup, 5))
             torch.cuda.empty_cache()
 
     offline = None
@@ -766,39 +791,42 @@ def main():
         offline = factorize_offline(cpu=not args.no_cpu)
         torch.cuda.empty_cache()
 
+    ts_us = main_rec["us_per_step"]
     line = {
         "metric": METRIC,
-        "value": round(w_bytes_gbs(main_sum), 1),
+        "value": main_rec["GB_per_s"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ts * 1e3, 6),
-        "us_per_step": main_sum["us_per_step"],
-        "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
+        "ms_per_step": round(ts_us * 1e-3, 6),
+        "us_per_step": ts_us,
+        "pct_of_hbm_peak": main_rec["pct_of_hbm_peak"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.act_dt == "bf16" else cfg.act_dt,
         "data": "synthetic (seeded N(0,1)/sqrt(dim) latents and factors; LLaVA-7B layer shapes)",
-        "config": {"workload": cfg.name, "shape": cfg.describe(), "splits": main_sum["splits"],
-                   "input_copies": main_sum["input_copies"], "timing": "hip-graph replay, cold HBM rotation"},
-        "roofline": roofline,
-        "warm_cache": main_sum["warm_cache"],
-        "cpu_baseline": cpu,
-        "parity_max_rel_err_vs_oracle": parity,
-        "vs_dense_flash_decoding": vs_dense,
-        "rotary_keys": rope_main,
+        "config": {"workload": cfg.name, "shape": cfg.describe(), "splits": main_rec["splits"],
+                   "input_copies": main_rec["input_copies"],
+                   "timing": "hip-graph replay of whole steps on one stream, cold HBM (>= 1 GiB touched per "
+                             "replay), median of timed regions of >= 1 ms",
+                   "step": ("append x.A_Kh / x.A_Vh of the new token, split decode, merge" if cfg.has_append
+                            else "split decode and merge")},
+        "timing": main_rec["timing"],
+        "roofline": main_rec["roofline"],
+        "warm_cache": main_rec["warm_cache"],
+        "cpu_baseline": main_rec.get("cpu_baseline"),
+        "parity_max_rel_err_vs_oracle": main_rec.get("parity_max_rel_err_vs_oracle"),
+        "vs_dense_flash_decoding": main_rec.get("vs_dense_flash_decoding"),
+        "rotary_keys": main_rec.get("rotary_keys"),
+        "append_alone": main_rec.get("append_alone"),
         "per_config": per,
         "shared_latent_ablation": ablation,
         "offline_factorize": offline,
         "kernel_src": kernel_src_hash(),
     }
     print(json.dumps(line), flush=True)
-
-
-def w_bytes_gbs(s):
-    return s["GB_per_s"]
 
 
 if __name__ == "__main__":
