@@ -37,7 +37,10 @@ constexpr int kLongTokens = 2048;       // per-split length cap for large batche
 constexpr long kLargeBatchPairs = 1024; // (b, h) pairs that make a batch "large"
 // Split grids at least this large merge in a second launch (measured on
 // MI355X: 8192 blocks gain 5.7 us from it, 160 blocks lose 1.35 us).
-constexpr long kSeparateMergeBlocks = 2048;
+#ifndef WSVD_SEPARATE_MERGE_BLOCKS
+#define WSVD_SEPARATE_MERGE_BLOCKS 2048
+#endif
+constexpr long kSeparateMergeBlocks = WSVD_SEPARATE_MERGE_BLOCKS;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -166,14 +169,23 @@ size_t wsvd_decode_workspace_bytes(int nb, int nh, int H, int L_cap, int n_split
     return wsvd_decode_lse_offset(nb, nh, H, L_cap, n_splits) + round_up((size_t)nb * nh * S * sizeof(float), 256);
 }
 
+// One append workspace serves both forms of the call at these sizes: the
+// bf16-operand kernel and the int8-operand kernel.
 size_t wsvd_append_counter_bytes(int nb, int nh, int r) {
     if (nb <= 0 || nh <= 0 || r <= 0) return 0;
-    return round_up((size_t)wsvd::append_num_tiles(nb, nh, r) * sizeof(unsigned), 256);
+    const int NT = wsvd::append_bf16_tile_cols(WSVD_BF16, r);
+    long tiles = wsvd::append_w8_num_tiles(nb, nh, r);
+    const long t = wsvd::append_bf16_num_tiles(nb, nh, r, NT);
+    if (t > tiles) tiles = t;
+    return round_up((size_t)tiles * sizeof(unsigned), 256);
 }
 
 size_t wsvd_append_workspace_bytes(int nb, int E, int nh, int r) {
     if (nb <= 0 || E <= 0 || nh <= 0 || r <= 0) return 0;
-    const size_t part = wsvd::append_partial_bytes(nb, E, nh, r);
+    const int NT = wsvd::append_bf16_tile_cols(WSVD_BF16, r);
+    size_t part = wsvd::append_w8_partial_bytes(nb, E, nh, r);
+    const size_t p = wsvd::append_bf16_partial_bytes(nb, E, nh, r, NT);
+    if (p > part) part = p;
     if (part == 0) return 0;
     return wsvd_append_counter_bytes(nb, nh, r) + round_up(part, 256);
 }
@@ -450,7 +462,6 @@ static wsvd::AppendArgs append_args(int nb, int E, int nh, int r, int L_cap, con
     a.C_dt = C_dt;
     a.s_K = s_K;
     a.s_V = s_V;
-    a.KS = wsvd::append_num_esplits(nb, E, nh, r);
     // Counters at byte 0 (one per output tile), then the partial tiles.
     const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
     a.counters = need > 0 ? static_cast<unsigned*>(workspace) : nullptr;
@@ -473,7 +484,7 @@ int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap, const int8_
                                        workspace_bytes, 512);
     if (st != WSVD_OK) return st;
     wsvd::AppendArgs a = append_args(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace);
-    a.KS = wsvd::append_num_esplits_w8(nb, E, nh, r);
+    a.KS = wsvd::append_w8_num_esplits(nb, E, nh, r);
     a.w8 = 1;
     a.x = xq;
     a.sx = sx;
@@ -481,7 +492,7 @@ int wsvd_append_latent_w8a8(int nb, int E, int nh, int r, int L_cap, const int8_
     a.A_V = AqT_V;
     a.sA_K = sA_K;
     a.sA_V = sA_V;
-    return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+    return wsvd::launch_append_w8(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
 int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, wsvd_dtype x_dt, const void* A_K,
@@ -496,10 +507,11 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     if (st != WSVD_OK) return st;
     wsvd::AppendArgs a = append_args(nb, E, nh, r, L_cap, pos, C_K, C_V, C_dt, s_K, s_V, workspace);
     a.w8 = 0;
+    a.KS = wsvd::append_bf16_num_esplits(nb, E, nh, r, wsvd::append_bf16_tile_cols(C_dt, r));
     a.x = x;
     a.A_K = A_K;
     a.A_V = A_V;
-    return wsvd::launch_append(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+    return wsvd::launch_append_bf16(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
 size_t wsvd_factorize_svd_workspace_bytes(int E, int nh, int H) {

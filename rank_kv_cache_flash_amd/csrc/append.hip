@@ -1,52 +1,30 @@
-// append.hip -- project each sequence's new token to its per-head latents and
-// write them into the latent caches.
+// append.hip -- the W8A8 form of the append: the new token's per-head latents
+// from int8 operands.  Per head h the cache row is x . A_Kh with A_Kh in
+// R^{E x r} ("WSVD: Weighted Low-Rank Approximation for Fast and Efficient
+// Execution of Low-Precision Vision-Language Models", Arabic page section
+// 2a, German page section 2A, Japanese page section 2.1); in the pages' W8A8
+// setting the low-rank layers run with 8-bit weights and activations after
+// an orthogonal Hadamard rotation S1 that smooths activation outliers
+// (German page section 2C, Italian page section 2C, Arabic page section 2c).
+// The bf16-operand append is append_stream.hip.
 //
-// Per head h the cache row is x . A_Kh with A_Kh in R^{E x r} ("WSVD:
-// Weighted Low-Rank Approximation for Fast and Efficient Execution of
-// Low-Precision Vision-Language Models", Arabic page section 2a, German page
-// section 2A, Japanese page section 2.1).  Stacking all heads gives one skinny
-// GEMM  P[nb, 2 nh r] = x[nb, E] . [A_K | A_V][E, 2 nh r]  (nb = 64, E = 4096,
-// 2 nh r = 3072 for the LLaVA-7B-shaped step): about 62 flop per byte of A,
-// under the MFMA ridge, so it is bound by streaming A from HBM.  It runs on
-// matrix cores (v_mfma_f32_16x16x32_bf16) so the arithmetic hides under
-// that stream.
+// x arrives as int8 codes of the Hadamard-rotated token with one fp32 scale
+// per token, A as int8 codes of the rotated factor, stored transposed
+// ([nh r, E], k-contiguous) with one fp32 scale per column.  Both operands
+// are k-contiguous, so both tiles are staged with whole-row loads and no
+// transpose, and v_mfma_i32_16x16x64_i8 accumulates exact int32 sums.
 //
 // One launch.  Block = 64 rows of x  x  64 columns of A  x  one E-slice;
-// enough E-slices (KS) are used to put >= 1.5 blocks on each CU.
-//  * A block requests two LDS stages (2 x 256 E rows of A and x) at once,
-//    one register buffer per stage.  With E = 4096 the split makes every
-//    slice exactly two stages, so the whole A stream is in flight at once
-//    and never waits on a dependent round trip.
-//  * A arrives row-major (columns contiguous) but the MFMA B operand wants 8
-//    consecutive k per lane, so each thread loads an 8 x 8 (k x n) bf16
-//    block with eight 16-byte loads (a wave covers 8 full 128-byte rows per
-//    load), transposes it in registers and stores 8 k-contiguous vectors
-//    into LDS.  The LDS tile is [64 n][256 k] with a 16-byte row pad and the
-//    k-block index xor-swizzled by n/8, so both the transposed stores and
-//    the fragment reads are free of bank conflicts.
-//  * x is read with whole-row loads (a wave covers two 512-byte row pieces
-//    per load) into a second padded LDS tile [64 m][256 k]; gathering the
-//    MFMA A fragments (16 rows x 16 bytes) straight from memory instead
-//    cost several times more L2 requests for the same bytes.
+// enough E-slices (KS) are used to put >= 1.5 blocks on each CU, each slice
+// at least two 512-k stages so a block requests a pair of stages at once.
 //  * Each wave owns 16 rows of x and all 64 columns: 4 accumulators of
 //    16 x 16.
-//  * With KS > 1 each block writes its fp32 partial tile to the workspace
-//    (device-coherent 16-byte stores, in the accumulator's own lane order,
-//    so a wave writes 1 KB contiguous per store) and bumps
-//    the tile's arrival counter; the block that arrives last sums the KS
-//    partials in slice order (so the result does not depend on which block
-//    finished last), resets the counter, rounds once to the cache dtype and
-//    writes row pos[b] of every head's K and V cache.
-//
-// W8A8 variant (w8): x arrives as int8 codes of the Hadamard-rotated token
-// with one fp32 scale per token, A as int8 codes of the rotated factor,
-// stored transposed ([nh r, E], k-contiguous) with one fp32 scale per
-// column (the pages' W8A8 setting with S1 outlier smoothing: German page
-// section 2C, Italian page section 2C, Arabic page section 2c).  Both
-// operands are k-contiguous, so both tiles are staged with whole-row loads
-// and no transpose, and v_mfma_i32_16x16x64_i8 accumulates exact int32
-// sums; the partial tiles are int32 (their sum is exact in any order).
-// The latent is acc * sx[b] * sA[n] in fp32, then stored as above.
+//  * With KS > 1 each block writes its int32 partial tile to the workspace
+//    (device-coherent 16-byte stores, in the accumulator's own lane order)
+//    and bumps the tile's arrival counter; the block that arrives last sums
+//    the KS partials (exact in any order), resets the counter, applies the
+//    scales, rounds once to the cache dtype and writes row pos[b] of every
+//    head's K and V cache.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
 
@@ -56,22 +34,14 @@
 
 namespace wsvd {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AP_NT = 64;           // columns per block
 constexpr int AP_MT = 64;           // rows of x per block
-constexpr int AP_EC = 256;          // E rows per LDS stage
-constexpr int AP_PITCH = AP_EC + 8; // bf16 elements per LDS row (16-byte pad)
-constexpr int AP_TILE_VALS = AP_NT * AP_MT;  // fp32 values in one partial tile
+constexpr int AP_TILE_VALS = AP_NT * AP_MT;  // int32 values in one partial tile
 
-union V16 {
-    u32x4 u;
-    bf16x8 b;
-};
-
-// One stage of operands in registers: this thread's 8 x 8 block of A and
-// its eight 16-byte pieces of x rows.
+// One stage of operands in registers: this thread's eight 16-byte pieces
+// of A rows and of x rows.
 struct Stage {
     u32x4 a[8];
     u32x4 x[8];
@@ -84,76 +54,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 constexpr int kNonTemporal = 2;     // cache-policy bit nt: streamed once
 constexpr int kCoherentAgent = 16;  // cache-policy bit sc1: device-coherent
 
-// Buffer loads keep one 32-bit lane offset per stream and put the uniform
-// part (stage start, row step) in a scalar offset, instead of a 64-bit
-// address per load.
-struct TileCtx {
-    __amdgpu_buffer_rsrc_t ra, rx;
-    uint32_t a_voff;     // bytes: (kblk * 8 * N1 + ncol) * 2
-    uint32_t a_row;      // bytes per row of A: N1 * 2
-    uint32_t x_voff[8];  // bytes: (xrow_i * E + xcol) * 2
-};
-
-__device__ __forceinline__ void load_stage(Stage& s, const TileCtx& c, int es) {
-    // Columns past N1 read column 0 and rows past nb read row nb - 1 instead
-    // (in bounds); those outputs are never written, and an output column
-    // (row) depends only on its own column of A (row of x).
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        s.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.a_voff, (es + i) * c.a_row, kNonTemporal);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s.x[i] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_voff[i], es * 2, 0);
-}
-
-// Transpose the stage's A block into LDS, stage x rows beside it, and run
-// the stage's MFMAs.
-__device__ __forceinline__ void mma_stage(const Stage& s, uint16_t* sB, uint16_t* sX, f32x4 (&acc)[4], int tid,
-                                          int lane, int wave) {
-    const int nblk = tid & 7;
-    const int kblk = tid >> 3;
-    // 8 x 8 transpose: tr[n'] holds k = 0..7 of column n'.
-    u32x4 tr[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t r0 = s.a[2 * p][w], r1 = s.a[2 * p + 1][w];
-            tr[2 * w][p] = (r0 & 0xffffu) | (r1 << 16);
-            tr[2 * w + 1][p] = (r0 >> 16) | (r1 & 0xffff0000u);
-        }
-    }
-    __syncthreads();  // the previous stage's fragment reads are done
-#pragma unroll
-    for (int np = 0; np < 8; ++np) {
-        const int n = nblk * 8 + np;
-        const int kb = kblk ^ (nblk & 7);
-        *reinterpret_cast<u32x4*>(&sB[n * AP_PITCH + kb * 8]) = tr[np];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(&sX[((tid >> 5) + 8 * i) * AP_PITCH + (tid & 31) * 8]) = s.x[i];
-    __syncthreads();
-    const uint16_t* xr = sX + (wave * 16 + (lane & 15)) * AP_PITCH + (lane >> 4) * 8;
-#pragma unroll
-    for (int st = 0; st < AP_EC / 32; ++st) {
-        V16 xf;
-        xf.u = *reinterpret_cast<const u32x4*>(xr + st * 32);
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-            const int n = jn * 16 + (lane & 15);
-            const int kb = (st * 4 + (lane >> 4)) ^ ((n >> 3) & 7);
-            V16 bf;
-            bf.u = *reinterpret_cast<const u32x4*>(&sB[n * AP_PITCH + kb * 8]);
-            acc[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf.b, bf.b, acc[jn], 0, 0, 0);
-        }
-    }
-}
-
-
 // ---- W8A8 operands: 512 k (bytes) per stage ---------------------------------
 constexpr int AP_ECB = 512;                 // int8 k per stage
-constexpr int AP_PITCHB = AP_ECB + 16;      // bytes per LDS row (same 528 as bf16)
-static_assert(AP_PITCHB == AP_PITCH * 2, "both variants share the LDS tiles");
+constexpr int AP_PITCHB = AP_ECB + 16;      // bytes per LDS row (16-byte pad)
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -240,10 +143,9 @@ __device__ __forceinline__ void store_int8_rows(const AppendArgs& a, const f32x4
     }
 }
 
-template <bool W8>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sB[AP_NT * AP_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t sX[AP_MT * AP_PITCH];
+__global__ __launch_bounds__(256) void append_w8_kernel(AppendArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t sB[AP_NT * AP_PITCHB];
+    __shared__ __attribute__((aligned(16))) uint8_t sX[AP_MT * AP_PITCHB];
     __shared__ int sh_last;
 
     const int N1 = a.nh * a.r;
@@ -253,48 +155,18 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int ks = blockIdx.z;
     const int e_len = a.E / a.KS;
     const int e_beg = ks * e_len;
-    const int ns = e_len / (W8 ? AP_ECB : AP_EC);
+    const int ns = e_len / AP_ECB;
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // acc holds fp32 sums, or (W8) the bits of exact int32 sums until the
-    // scales are applied after the split-E reduction.
+    // acc holds the bits of exact int32 sums until the scales are applied
+    // after the split-E reduction.
     f32x4 acc[4];
     Stage s0, s1;
-    if constexpr (!W8) {
-        TileCtx c;
-        c.ra = make_rsrc(kv ? a.A_V : a.A_K, (uint32_t)((size_t)a.E * N1 * 2));
-        c.rx = make_rsrc(a.x, (uint32_t)((size_t)a.nb * a.E * 2));
-        int ncol = n0 + (tid & 7) * 8;
-        if (ncol >= N1) ncol = 0;  // N1 is a multiple of 16, chunks are 8 wide
-        c.a_row = (uint32_t)N1 * 2u;
-        c.a_voff = ((uint32_t)(tid >> 3) * 8u * (uint32_t)N1 + (uint32_t)ncol) * 2u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            c.x_voff[i] = ((uint32_t)min(m0 + (tid >> 5) + 8 * i, a.nb - 1) * (uint32_t)a.E + (tid & 31) * 8u) * 2u;
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Two stages (512 E rows) requested together; the split factor keeps
-        // a block's slice at one or two stages, so one pass normally covers it.
-        // Pairs are requested without a branch between them (an odd last
-        // stage goes alone): behind a branch, the waits for the first stage
-        // would also wait for the second, so its MFMAs could not overlap the
-        // second stage's flight.
-        int st = 0;
-        for (; st + 1 < ns; st += 2) {
-            load_stage(s0, c, e_beg + st * AP_EC);
-            load_stage(s1, c, e_beg + (st + 1) * AP_EC);
-            mma_stage(s0, sB, sX, acc, tid, lane, wave);
-            mma_stage(s1, sB, sX, acc, tid, lane, wave);
-        }
-        if (st < ns) {
-            load_stage(s0, c, e_beg + st * AP_EC);
-            mma_stage(s0, sB, sX, acc, tid, lane, wave);
-        }
-    } else {
+    {
         TileCtxW8 c;
         c.ra = make_rsrc(kv ? a.A_V : a.A_K, (uint32_t)((size_t)a.E * N1));
         c.rx = make_rsrc(a.x, (uint32_t)((size_t)a.nb * a.E));
@@ -307,8 +179,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         i32x4 iacc[4];
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) iacc[jn] = i32x4{0, 0, 0, 0};
-        uint8_t* bB = reinterpret_cast<uint8_t*>(sB);
-        uint8_t* bX = reinterpret_cast<uint8_t*>(sX);
+        uint8_t* bB = sB;
+        uint8_t* bX = sX;
         int st = 0;
         for (; st + 1 < ns; st += 2) {
             load_stage_w8(s0, c, e_beg + st * AP_ECB);
@@ -327,19 +199,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     // Rows of the caches this lane's accumulator entries go to (requested
     // only once the tile is complete, beside the last round of loads).
     int prow[4];
-    float xs[4], as[4];  // W8: this lane's row and column scales
+    float xs[4], as[4];  // this lane's row and column scales
     auto load_pos = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = m0 + wave * 16 + (lane >> 4) * 4 + i;
             prow[i] = (m < a.nb) ? a.pos[m] : -1;
-            if constexpr (W8) xs[i] = a.sx[min(m, a.nb - 1)];
+            xs[i] = a.sx[min(m, a.nb - 1)];
         }
-        if constexpr (W8) {
-            const float* sA = kv ? a.sA_V : a.sA_K;
+        const float* sA = kv ? a.sA_V : a.sA_K;
 #pragma unroll
-            for (int jn = 0; jn < 4; ++jn) as[jn] = sA[min(n0 + jn * 16 + (lane & 15), N1 - 1)];
-        }
+        for (int jn = 0; jn < 4; ++jn) as[jn] = sA[min(n0 + jn * 16 + (lane & 15), N1 - 1)];
     };
 
     if (a.KS > 1) {
@@ -381,13 +251,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             for (int u = 0; u < 8; ++u) {
                 if (k0 + u < a.KS) {
 #pragma unroll
-                    for (int jn = 0; jn < 4; ++jn) {
-                        if constexpr (W8)
-                            sum[jn] = __builtin_bit_cast(f32x4, __builtin_bit_cast(i32x4, sum[jn]) +
-                                                                    __builtin_bit_cast(i32x4, v[u][jn]));
-                        else
-                            sum[jn] += v[u][jn];
-                    }
+                    for (int jn = 0; jn < 4; ++jn)
+                        sum[jn] = __builtin_bit_cast(f32x4, __builtin_bit_cast(i32x4, sum[jn]) +
+                                                                __builtin_bit_cast(i32x4, v[u][jn]));
                 }
             }
         }
@@ -397,7 +263,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     } else {
         load_pos();
     }
-    if constexpr (W8) {  // exact integer sums -> latent values
+    {  // exact integer sums -> latent values
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) {
             const i32x4 q = __builtin_bit_cast(i32x4, acc[jn]);
@@ -429,44 +295,32 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
 }
 
-int append_num_esplits(int nb, int E, int nh, int r) {
-    const long ntile = append_num_tiles(nb, nh, r);
-    int ks = 1;
-    // >= 1.5 blocks per CU (256 CUs); every E-slice a whole number of the
-    // larger (int8, 512 k) stage, so both variants split the same way and
-    // share one workspace size.
-    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2 * ks * AP_ECB) == 0) ks *= 2;
-    return ks;
+long append_w8_num_tiles(int nb, int nh, int r) {
+    return (long)((nh * r + AP_NT - 1) / AP_NT) * 2 * ((nb + AP_MT - 1) / AP_MT);
 }
 
-// The int8 operands' slices: the same split halved while a slice would hold
-// a single 512-k stage, so each block requests a pair of stages at once
-// (measured on MI355X at the 64 x 4096 -> 32 x 48 shape: 17.5 against
-// 18.5 us with the quantiser).  Never more slices than the bf16 split, so
-// the workspace sized for that split covers it.
-int append_num_esplits_w8(int nb, int E, int nh, int r) {
-    int ks = append_num_esplits(nb, E, nh, r);
+// E slices of the int8-operand kernel: >= 1.5 blocks per CU (256 CUs) while
+// every slice stays at least two 512-k stages, so each block requests a pair
+// of stages at once (measured on MI355X at the 64 x 4096 -> 32 x 48 shape:
+// 17.5 against 18.5 us with the quantiser).
+int append_w8_num_esplits(int nb, int E, int nh, int r) {
+    const long ntile = append_w8_num_tiles(nb, nh, r);
+    int ks = 1;
+    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2 * ks * AP_ECB) == 0) ks *= 2;
     while (ks > 1 && E / ks < 2 * AP_ECB) ks /= 2;
     return ks;
 }
 
-long append_num_tiles(int nb, int nh, int r) {
-    return (long)((nh * r + AP_NT - 1) / AP_NT) * 2 * ((nb + AP_MT - 1) / AP_MT);
-}
-
-size_t append_partial_bytes(int nb, int E, int nh, int r) {
-    const int ks = append_num_esplits(nb, E, nh, r);
+size_t append_w8_partial_bytes(int nb, int E, int nh, int r) {
+    const int ks = append_w8_num_esplits(nb, E, nh, r);
     if (ks <= 1) return 0;
-    return (size_t)append_num_tiles(nb, nh, r) * ks * AP_TILE_VALS * sizeof(float);
+    return (size_t)append_w8_num_tiles(nb, nh, r) * ks * AP_TILE_VALS * sizeof(int32_t);
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+hipError_t launch_append_w8(const AppendArgs& a, hipStream_t st) {
     const int N1 = a.nh * a.r;
     dim3 g((N1 + AP_NT - 1) / AP_NT, 2 * ((a.nb + AP_MT - 1) / AP_MT), a.KS);
-    if (a.w8)
-        hipLaunchKernelGGL(append_kernel<true>, g, dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL(append_kernel<false>, g, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(append_w8_kernel, g, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -63,12 +63,25 @@ struct AppendArgs {
     int C_dt;
     uint16_t* s_K;        // fp16 [nb, nh, L_cap] row scales (int8 caches only)
     uint16_t* s_V;
-    float* part;          // fp32 split-E partial tiles (KS > 1 only)
+    float* part;          // split-E partial tiles (KS > 1 only): fp32, or int32 for w8
     unsigned* counters;   // per-tile arrival counters, zero between calls
     int KS;               // number of E splits
 };
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+// bf16 operands (append_stream.hip): x [nb, E] and A [E, nh*r] bf16.
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t st);
+// Its column tile (32, or 64 for int8 caches of rank 64), tile count, E
+// slices and partial-tile bytes (0 when E is not split) (host).
+int append_bf16_tile_cols(int C_dt, int r);
+long append_bf16_num_tiles(int nb, int nh, int r, int NT);
+int append_bf16_num_esplits(int nb, int E, int nh, int r, int NT);
+size_t append_bf16_partial_bytes(int nb, int E, int nh, int r, int NT);
+
+// int8 operands (append.hip): x codes [nb, E] + sx, A^T codes [nh*r, E] + sA.
+hipError_t launch_append_w8(const AppendArgs& a, hipStream_t st);
+long append_w8_num_tiles(int nb, int nh, int r);
+int append_w8_num_esplits(int nb, int E, int nh, int r);
+size_t append_w8_partial_bytes(int nb, int E, int nh, int r);
 
 // W8A8 helpers (w8a8.hip): S1 rotation + per-row int8 codes of activations,
 // and the offline rotation + per-column int8 codes of a factor.
@@ -77,15 +90,6 @@ hipError_t launch_w8a8_quantize_rows(int nb, int E, const void* x, int x_dt, int
 hipError_t launch_w8a8_prepare(int E, int N, const void* A, int A_dt, int8_t* AqT, float* sA, hipStream_t st);
 // Columns of A one prepare block rotates at once (LDS holds cols * E floats).
 int w8a8_prepare_cols(int E);
-
-// Split-E factor the append kernel uses for these sizes (host).
-int append_num_esplits(int nb, int E, int nh, int r);
-// The int8-operand variant's split (never more slices than the one above).
-int append_num_esplits_w8(int nb, int E, int nh, int r);
-// Output tiles (64 rows x 64 columns, K and V separately) (host).
-long append_num_tiles(int nb, int nh, int r);
-// Bytes of split-E partial tiles for these sizes, 0 when KS == 1 (host).
-size_t append_partial_bytes(int nb, int E, int nh, int r);
 
 // Offline per-head factorisation (factorize.hip).  Truncated SVD: Gram
 // partials into Gpart ([chunks, nh, H, H] fp64), Jacobi per head, then
