@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "wsvd_common.hpp"
@@ -42,6 +43,19 @@ constexpr long kLargeBatchPairs = 1024; // (b, h) pairs that make a batch "large
 #endif
 constexpr long kSeparateMergeBlocks = WSVD_SEPARATE_MERGE_BLOCKS;
 
+// a * b * ... <= limit for non-negative factors, without overflowing (a
+// product of several int sizes can pass 2^63).
+bool product_le(std::initializer_list<long long> factors, long long limit) {
+    long long p = 1;
+    for (long long v : factors) {
+        if (v < 0) return false;
+        if (v == 0) return 0 <= limit;
+        if (p > limit / v) return false;
+        p *= v;
+    }
+    return p <= limit;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -53,7 +67,7 @@ bool rank_ok(int r) { return r == 16 || r == 32 || r == 48 || r == 64; }
 // The split kernel addresses one (b, h)'s rows with 32-bit byte offsets.
 bool rows_fit(int L_cap, int row_elems, int dt) {
     const long long es = dt == WSVD_F32 ? 4 : dt == WSVD_I8 ? 1 : 2;
-    return (long long)L_cap * row_elems * es < (1ll << 31);
+    return product_le({L_cap, row_elems, es}, (1ll << 31) - 1);
 }
 
 int resolve_splits(int nb, int nh, int L_cap, int n_splits) {
@@ -63,10 +77,10 @@ int resolve_splits(int nb, int nh, int L_cap, int n_splits) {
     long s = 1;
     if (bh < kFillBlocks) {
         s = (kFillBlocks + bh - 1) / bh;
-        const long smax = (L_cap + kMinSplitTokens - 1) / kMinSplitTokens;
+        const long smax = ((long)L_cap + kMinSplitTokens - 1) / kMinSplitTokens;
         if (s > smax) s = smax;
     } else if (bh >= kLargeBatchPairs) {
-        s = (L_cap + kLongTokens - 1) / kLongTokens;
+        s = ((long)L_cap + kLongTokens - 1) / kLongTokens;
     }
     if (s < 1) s = 1;
     return (int)s;
@@ -213,7 +227,7 @@ static int check_decode(int nb, int nh, int H, int r, int L_cap, const int32_t* 
                         const void* B_K, const void* B_V, wsvd_dtype B_dt, float softmax_scale, int n_splits,
                         void* out, wsvd_dtype out_dt, wsvd::DecodeArgs& a) {
     if (nb <= 0 || nh <= 0 || H <= 0 || r <= 0 || L_cap <= 0 || n_splits < 0 || r > H) return WSVD_ERR_SHAPE;
-    if ((long long)nb * nh * L_cap * r > (1ll << 46)) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, nh, L_cap, r}, 1ll << 46)) return WSVD_ERR_SHAPE;
     if (!L || !q || !C_K || !C_V || !B_K || !B_V) return WSVD_ERR_NULL;
     if (!act_dtype_ok(q_dt) || !act_dtype_ok(B_dt) || !cache_dtype_ok(C_dt)) return WSVD_ERR_DTYPE;
     if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
@@ -226,7 +240,7 @@ static int check_decode(int nb, int nh, int H, int r, int L_cap, const int32_t* 
     if (C_dt == WSVD_I8 && (!aligned16(s_K) || !aligned16(s_V))) return WSVD_ERR_ALIGN;
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0) return WSVD_ERR_SHAPE;
-    if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, nh, S}, (1ll << 31) - 1)) return WSVD_ERR_SHAPE;
 
     memset(&a, 0, sizeof(a));
     a.nb = nb;
@@ -300,7 +314,7 @@ int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap, const int32_t* L, c
                            void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt,
                            hipStream_t stream) {
     if (nb <= 0 || nh <= 0 || H <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
-    if ((long long)nb * nh * L_cap * H > (1ll << 46)) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, nh, L_cap, H}, 1ll << 46)) return WSVD_ERR_SHAPE;
     if (!L || !q || !K || !V) return WSVD_ERR_NULL;
     if (!act_dtype_ok(q_dt) || kv_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
     if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
@@ -310,7 +324,7 @@ int wsvd_dense_decode_attn(int nb, int nh, int H, int L_cap, const int32_t* L, c
         return WSVD_ERR_ALIGN;
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0) return WSVD_ERR_SHAPE;
-    if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, nh, S}, (1ll << 31) - 1)) return WSVD_ERR_SHAPE;
     const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
     if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
 
@@ -350,7 +364,7 @@ int wsvd_decode_attn_rope(int nb, int nh, int H, int r, int L_cap, const int32_t
                           float softmax_scale, int n_splits, void* workspace, size_t workspace_bytes, void* out,
                           wsvd_dtype out_dt, hipStream_t stream) {
     if (nb <= 0 || nh <= 0 || H <= 0 || r <= 0 || L_cap <= 0 || n_splits < 0 || r > H) return WSVD_ERR_SHAPE;
-    if ((long long)nb * nh * L_cap * r > (1ll << 46)) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, nh, L_cap, r}, 1ll << 46)) return WSVD_ERR_SHAPE;
     if (!L || !q || !C_K || !C_V || !B_K || !B_V || !rope_cos || !rope_sin) return WSVD_ERR_NULL;
     if (!act_dtype_ok(q_dt) || B_dt != WSVD_BF16 || C_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
     if (out && !act_dtype_ok(out_dt)) return WSVD_ERR_DTYPE;
@@ -360,7 +374,7 @@ int wsvd_decode_attn_rope(int nb, int nh, int H, int r, int L_cap, const int32_t
         return WSVD_ERR_ALIGN;
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0) return WSVD_ERR_SHAPE;
-    if ((long long)nb * nh * S >= (1ll << 31)) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, nh, S}, (1ll << 31) - 1)) return WSVD_ERR_SHAPE;
     const size_t need = wsvd_decode_workspace_bytes(nb, nh, H, L_cap, n_splits);
     if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
 
@@ -439,8 +453,8 @@ static int check_append_common(int nb, int E, int nh, int r, int L_cap, const in
         return WSVD_ERR_SHAPE;
     }
     if (!rank_ok(r) || E % e_multiple != 0) return WSVD_ERR_UNSUPPORTED;
-    if ((long long)nb * nh * L_cap * r > (1ll << 46) || (long long)E * nh * r > (1ll << 30) ||
-        (long long)nb * E > (1ll << 30))
+    if (!product_le({nb, nh, L_cap, r}, 1ll << 46) || !product_le({E, nh, r}, 1ll << 30) ||
+        !product_le({nb, E}, 1ll << 30))
         return WSVD_ERR_SHAPE;
     if (!aligned16(pos) || !aligned16(C_K) || !aligned16(C_V)) return WSVD_ERR_ALIGN;
     const size_t need = wsvd_append_workspace_bytes(nb, E, nh, r);
@@ -522,7 +536,7 @@ size_t wsvd_factorize_svd_workspace_bytes(int E, int nh, int H) {
 int wsvd_factorize_svd(int E, int nh, int H, int r, const float* W, float* A, float* B, float* sigma, int* sweeps,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (E <= 0 || nh <= 0 || r <= 0 || H <= 0 || r > H) return WSVD_ERR_SHAPE;
-    if (nh > 65535 || (long long)E * nh * H > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (nh > 65535 || !product_le({E, nh, H}, 1ll << 40)) return WSVD_ERR_SHAPE;
     if (!head_dim_ok(H)) return WSVD_ERR_UNSUPPORTED;
     if (!W || !A || !B || !sigma) return WSVD_ERR_NULL;
     if (!aligned16(W) || !aligned16(A) || !aligned16(B) || !aligned16(sigma)) return WSVD_ERR_ALIGN;
@@ -537,7 +551,7 @@ int wsvd_factorize_svd(int E, int nh, int H, int r, const float* W, float* A, fl
 static int check_weighted(int E, int nh, int H, int r, const float* W, const float* F, const float* in,
                           const float* out) {
     if (E <= 0 || nh <= 0 || r <= 0 || H <= 0 || r > H) return WSVD_ERR_SHAPE;
-    if (nh > 65535 || (long long)E * nh * H > (1ll << 40)) return WSVD_ERR_SHAPE;
+    if (nh > 65535 || !product_le({E, nh, H}, 1ll << 40)) return WSVD_ERR_SHAPE;
     if (!head_dim_ok(H) || !rank_ok(r)) return WSVD_ERR_UNSUPPORTED;
     if (!W || !F || !in || !out) return WSVD_ERR_NULL;
     if (!aligned16(W) || !aligned16(F) || !aligned16(in) || !aligned16(out)) return WSVD_ERR_ALIGN;
@@ -582,7 +596,7 @@ int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap, const int32
                             int n_splits, void* workspace, size_t workspace_bytes, void* out, wsvd_dtype out_dt,
                             hipStream_t stream) {
     if (nb <= 0 || nh <= 0 || H <= 0 || R <= 0 || L_cap <= 0 || n_splits < 0) return WSVD_ERR_SHAPE;
-    if (nh > 4096 || (long long)nb * L_cap * R > (1ll << 40) || (long long)R * nh * H > (1ll << 40))
+    if (nh > 4096 || !product_le({nb, L_cap, R}, 1ll << 40) || !product_le({R, nh, H}, 1ll << 40))
         return WSVD_ERR_SHAPE;
     if (!L || !q || !C_K || !C_V || !B_K || !B_V || !out) return WSVD_ERR_NULL;
     if (out_dt != WSVD_F32 && out_dt != WSVD_BF16) return WSVD_ERR_DTYPE;
@@ -592,7 +606,7 @@ int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap, const int32
         return WSVD_ERR_ALIGN;
     const int S = resolve_splits(nb, nh, L_cap, n_splits);
     if (S <= 0) return WSVD_ERR_SHAPE;
-    if ((long long)nb * S * nh > (1ll << 31) - 4096) return WSVD_ERR_SHAPE;
+    if (!product_le({nb, S, nh}, (1ll << 31) - 4096)) return WSVD_ERR_SHAPE;
     const size_t need = wsvd_shared_decode_workspace_bytes(nb, nh, R, L_cap, n_splits);
     if (!workspace || !aligned256(workspace) || workspace_bytes < need) return WSVD_ERR_WORKSPACE;
     wsvd::SharedArgs a;

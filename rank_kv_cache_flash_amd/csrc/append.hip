@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void append_w8_kernel(AppendArgs a) {
 }
 
 long append_w8_num_tiles(int nb, int nh, int r) {
-    return (long)((nh * r + AP_NT - 1) / AP_NT) * 2 * ((nb + AP_MT - 1) / AP_MT);
+    return (((long)nh * r + AP_NT - 1) / AP_NT) * 2 * (((long)nb + AP_MT - 1) / AP_MT);
 }
 
 // E slices of the int8-operand kernel: >= 1.5 blocks per CU (256 CUs) while
@@ -306,7 +306,7 @@ long append_w8_num_tiles(int nb, int nh, int r) {
 int append_w8_num_esplits(int nb, int E, int nh, int r) {
     const long ntile = append_w8_num_tiles(nb, nh, r);
     int ks = 1;
-    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2 * ks * AP_ECB) == 0) ks *= 2;
+    while (ntile * ks < WSVD_APPEND_TARGET_BLOCKS && E % (2L * ks * AP_ECB) == 0) ks *= 2;
     while (ks > 1 && E / ks < 2 * AP_ECB) ks /= 2;
     return ks;
 }

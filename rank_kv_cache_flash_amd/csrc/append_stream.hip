@@ -365,14 +365,14 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
 int append_bf16_tile_cols(int C_dt, int r) { (void)C_dt; (void)r; return 64; }
 
 long append_bf16_num_tiles(int nb, int nh, int r, int NT) {
-    return (long)((nh * r + NT - 1) / NT) * 2 * ((nb + kRows - 1) / kRows);
+    return (((long)nh * r + NT - 1) / NT) * 2 * (((long)nb + kRows - 1) / kRows);
 }
 
 // Fewest E slices (whole 256-row stages, halving) that give >= 160 blocks.
 int append_bf16_num_esplits(int nb, int E, int nh, int r, int NT) {
     const long nt = append_bf16_num_tiles(nb, nh, r, NT);
     int ks = 1;
-    while (nt * ks < kTargetBlocks && E % (2 * ks * kStageK) == 0) ks *= 2;
+    while (nt * ks < kTargetBlocks && E % (2L * ks * kStageK) == 0) ks *= 2;
     return ks;
 }
 

@@ -586,19 +586,20 @@ __global__ __launch_bounds__(256) void als_cols_kernel(const float* __restrict__
 
 int svd_num_chunks(int E, int nh) {
     // Enough (chunk, head) blocks to cover the CUs twice; at least 64 rows each.
-    int c = (512 + nh - 1) / nh;
-    const int cmax = (E + 63) / 64;
+    // (64-bit intermediates: E and nh may be any positive int here.)
+    long c = (512L + nh - 1) / nh;
+    const long cmax = ((long)E + 63) / 64;
     if (c > cmax) c = cmax;
     if (c < 1) c = 1;
-    int rows = (E + c - 1) / c;
+    long rows = ((long)E + c - 1) / c;
     rows = (rows + kGramRows - 1) / kGramRows * kGramRows;
-    return (E + rows - 1) / rows;
+    return (int)(((long)E + rows - 1) / rows);
 }
 
 static int svd_rows_per_chunk(int E, int nh) {
-    const int c = svd_num_chunks(E, nh);
-    int rows = (E + c - 1) / c;
-    return (rows + kGramRows - 1) / kGramRows * kGramRows;
+    const long c = svd_num_chunks(E, nh);
+    const long rows = ((long)E + c - 1) / c;
+    return (int)((rows + kGramRows - 1) / kGramRows * kGramRows);
 }
 
 hipError_t launch_factorize_svd(const float* W, int E, int nh, int H, int r, float* A, float* B, float* sigma,
