@@ -531,6 +531,24 @@ def cpu_baseline(w, gpu_out, budget_s=12.0):
 
 
 # ---------------------------------------------------------------------------
+def launch_floors(blocks, nbytes, steps, warmup):
+    """What a launch on the decode's grid cannot beat on this device, timed
+    like the step: an empty kernel, and a stream of the same bytes with every
+    request issued at once (wsvd_floor_probe), rotating copies over >= 1 GiB."""
+    import torch
+    from rank_kv_cache_flash_amd import wsvd
+    sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    copies = max(1, min(256, math.ceil(COLD_BYTES / nbytes)))
+    srcs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    t_empty = graph_time(lambda i: wsvd.floor_probe(0, blocks, sink), steps, warmup)
+    t_stream = graph_time(lambda i: wsvd.floor_probe(1, blocks, sink, srcs[i % copies]), steps, warmup, copies)
+    del srcs
+    return {"grid_blocks": blocks, "bytes": int(nbytes), "empty_launch_us": round(t_empty * 1e6, 3),
+            "stream_us": round(t_stream * 1e6, 3), "stream_GB_per_s": round(nbytes / t_stream / 1e9, 1),
+            "note": "wsvd_floor_probe on the decode's grid: empty kernel, and the same bytes streamed with all "
+                    "requests issued at once; graph replay, cold HBM"}
+
+
 def measure(cfg, steps, warmup, n_splits=None, cpu_budget=None, extras=True):
     """One workload: the whole step (append when the workload has one, split
     decode, merge), the dominant kernel alone for the roofline, a labelled
@@ -567,6 +585,10 @@ def measure(cfg, steps, warmup, n_splits=None, cpu_budget=None, extras=True):
         "warm_cache": {"us_per_step": round(tw * 1e6, 3), "GB_per_s": round(w.step_bytes / tw / 1e9, 1),
                        "note": "every step on one input copy (cache-resident where it fits); not an HBM figure"},
     }
+    blocks = cfg.nb * cfg.nh * w.S
+    fb = w.decode_kernel_bytes // (16 * blocks) * 16 * blocks
+    if 0 < fb // (16 * blocks) <= 4096:
+        rec["floors"] = launch_floors(blocks, fb, steps, warmup)
     if cpu_budget:
         torch.cuda.synchronize()
         rec["cpu_baseline"], rec["parity_max_rel_err_vs_oracle"] = cpu_baseline(w, w.out, budget_s=cpu_budget)
@@ -597,6 +619,8 @@ def main():
     ap.add_argument("--also", default="2,3,4", help="other workloads measured into per_config ('' for none)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="skip the dense, rotary and append-alone comparisons")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle seconds for the headline workload")
     ap.add_argument("--cpu-budget-other", type=float, default=4.0, help="oracle seconds for each other workload")
     ap.add_argument("--mode", choices=["bench", "decode-loop", "step-loop", "copy-calib", "counters", "dense-sweep",
@@ -766,7 +790,7 @@ def main():
 
     cfg = CONFIGS[args.config]
     main_rec = measure(cfg, args.steps, args.warmup, n_splits=args.splits or None,
-                       cpu_budget=None if args.no_cpu else args.cpu_budget)
+                       cpu_budget=None if args.no_cpu else args.cpu_budget, extras=args.extras)
 
     per = {}
     also = [int(x) for x in args.also.split(",") if x.strip()] if args.also else []
@@ -775,7 +799,7 @@ def main():
             continue
         c = CONFIGS[cid]
         per[c.name] = measure(c, args.steps, min(args.warmup, 10),
-                              cpu_budget=None if args.no_cpu else args.cpu_budget_other)
+                              cpu_budget=None if args.no_cpu else args.cpu_budget_other, extras=args.extras)
         per[c.name]["steps"] = args.steps
         torch.cuda.empty_cache()
 
@@ -816,6 +840,7 @@ def main():
         "timing": main_rec["timing"],
         "roofline": main_rec["roofline"],
         "warm_cache": main_rec["warm_cache"],
+        "floors": main_rec.get("floors"),
         "cpu_baseline": main_rec.get("cpu_baseline"),
         "parity_max_rel_err_vs_oracle": main_rec.get("parity_max_rel_err_vs_oracle"),
         "vs_dense_flash_decoding": main_rec.get("vs_dense_flash_decoding"),

@@ -481,6 +481,19 @@ int wsvd_shared_decode_attn(int nb, int nh, int H, int R, int L_cap,
                             void* workspace, size_t workspace_bytes,
                             void* out, wsvd_dtype out_dt, hipStream_t stream);
 
+/*
+ * wsvd_floor_probe -- measurement aid, not part of the decode path: the
+ * floor a decode launch of `blocks` workgroups of 256 threads cannot beat on
+ * this device.  mode 0 launches an empty kernel (sink: float [blocks], read
+ * and possibly written); mode 1 streams `bytes` of src (16-byte aligned,
+ * split evenly into whole 16-byte chunks per block, at most 4096 chunks per
+ * block), every request issued before any is used, and stores one value per
+ * block into sink.  A small decode step (for example 5 MB for one 32-head
+ * layer of 1088 tokens) is bound by these, not by HBM bandwidth.
+ * WSVD_ERR_SHAPE for a bad mode, grid or byte count.
+ */
+int wsvd_floor_probe(int mode, int blocks, const void* src, size_t bytes, float* sink, hipStream_t stream);
+
 /* Static description of a status code.  Pure host; never NULL. */
 const char* wsvd_status_string(int status);
 

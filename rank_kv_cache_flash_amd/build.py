@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwsvd.so")
 
-SOURCES = ["abi.hip", "decode.hip", "decode_bf16_r32.hip", "decode_rope.hip", "combine.hip", "append.hip", "append_stream.hip", "w8a8.hip", "factorize.hip", "shared_decode.hip"]
+SOURCES = ["abi.hip", "decode.hip", "decode_bf16_r32.hip", "decode_rope.hip", "combine.hip", "append.hip", "append_stream.hip", "w8a8.hip", "factorize.hip", "shared_decode.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

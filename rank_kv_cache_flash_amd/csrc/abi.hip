@@ -528,6 +528,16 @@ int wsvd_append_latent(int nb, int E, int nh, int r, int L_cap, const void* x, w
     return wsvd::launch_append_bf16(a, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
 }
 
+int wsvd_floor_probe(int mode, int blocks, const void* src, size_t bytes, float* sink, hipStream_t stream) {
+    if ((mode != 0 && mode != 1) || blocks <= 0 || blocks > (1 << 20)) return WSVD_ERR_SHAPE;
+    if (!sink || (mode == 1 && !src)) return WSVD_ERR_NULL;
+    if (!aligned16(sink) || (mode == 1 && !aligned16(src))) return WSVD_ERR_ALIGN;
+    // mode 1: at most 16 loads of 16 bytes per thread, whole 16-byte chunks per block
+    if (mode == 1 && (bytes == 0 || bytes % (16 * (size_t)blocks) != 0 || bytes / 16 / (size_t)blocks > 16 * 256))
+        return WSVD_ERR_SHAPE;
+    return wsvd::launch_probe(mode, blocks, src, bytes, sink, stream) == hipSuccess ? WSVD_OK : WSVD_ERR_HIP;
+}
+
 size_t wsvd_factorize_svd_workspace_bytes(int E, int nh, int H) {
     if (E <= 0 || nh <= 0 || !head_dim_ok(H)) return 0;
     return (size_t)wsvd::svd_num_chunks(E, nh) * nh * H * H * sizeof(double);

@@ -44,6 +44,10 @@ hipError_t launch_dense_split(const DecodeArgs& a, int H, hipStream_t st);
 
 hipError_t launch_combine(int nb, int nh, int H, int S, const float* o_part, const float* lse_part,
                           void* out, int out_dt, hipStream_t st);
+// Measurement floors (probe.hip): mode 0 an empty launch, mode 1 a stream of
+// `bytes` from src split evenly over `blocks` blocks of 256 threads.
+hipError_t launch_probe(int mode, int blocks, const void* src, size_t bytes, float* sink, hipStream_t st);
+
 // p[0 .. n) = 0 (uint32 words), one small launch.
 hipError_t launch_fill_zero_u32(unsigned* p, size_t n, hipStream_t st);
 

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.wsvd_shared_decode_attn.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, i32, vp, sz, vp, i32,
                                           vp]
     L.wsvd_shared_decode_attn.restype = i32
+    L.wsvd_floor_probe.argtypes = [i32, i32, vp, sz, vp, vp]
+    L.wsvd_floor_probe.restype = i32
     L.wsvd_status_string.argtypes = [i32]
     L.wsvd_status_string.restype = ctypes.c_char_p
     L.wsvd_version.argtypes = []
@@ -667,6 +669,21 @@ def shared_decode_attn(q, C_K, C_V, B_K, B_V, L, *, softmax_scale=None, n_splits
                                        _stream(stream))
     _check(st, "wsvd_shared_decode_attn")
     return out
+
+
+def floor_probe(mode, blocks, sink, src=None, stream=None):
+    """wsvd_floor_probe: mode 0 an empty launch of `blocks` x 256 threads,
+    mode 1 a stream of all of src (uint8, contiguous) over the same grid;
+    sink float32 [blocks]."""
+    if sink is None or sink.dtype != torch.float32 or sink.numel() < blocks:
+        raise ValueError(f"sink must be float32 with at least {blocks} elements")
+    if src is not None and src.dim() != 1:
+        raise ValueError("src must be a 1-d byte tensor")
+    _dev(sink, "sink")
+    _dev(src, "src")
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    _check(lib().wsvd_floor_probe(int(mode), int(blocks), _ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "wsvd_floor_probe")
 
 
 def shared_device_inputs(inp, device="cuda"):

@@ -431,3 +431,13 @@ def noalloc(L, **kw):
 ])
 def test_decode_noalloc_rejects(L, kw, want):
     assert noalloc(L, **kw) == want
+
+
+@pytest.mark.parametrize("mode,blocks,src,nbytes,sink,want", [
+    (2, 160, P, 2560, P, ESHAPE), (0, 0, None, 0, P, ESHAPE), (0, 160, None, 0, None, ENULL),
+    (1, 160, None, 2560, P, ENULL), (1, 160, P + 8, 2560, P, EALIGN), (1, 160, P, 2570, P, ESHAPE),
+    (1, 160, P, 160 * 16 * 4097, P, ESHAPE), (1, 160, P, 0, P, ESHAPE),
+])
+def test_floor_probe_rejects(L, mode, blocks, src, nbytes, sink, want):
+    v = ctypes.c_void_p
+    assert L.wsvd_floor_probe(mode, blocks, v(src), nbytes, v(sink), None) == want
