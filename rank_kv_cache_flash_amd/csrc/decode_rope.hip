@@ -11,7 +11,7 @@
 // rebuilds each key tile on matrix cores and rotates it in registers.
 //
 // Per (b, h, split) workgroup of 4 waves; a wave takes 16-row tiles (tile
-// k of wave w starts at row 16 w + 64 k of the split), two tiles in flight.
+// k of wave w starts at row 16 w + 64 k of the split), D = 2 tiles in flight.
 //  * K tile: v_mfma_f32_16x16x32_bf16 with the 16 latent rows as the A
 //    operand (lane l: row l % 16, 8 consecutive ranks at 8 (l / 16)), read
 //    straight from the cache, and B_Kh as the B operand: staged transposed
@@ -19,13 +19,21 @@
 //    registers for the split (r H / 512 u32x4 per lane), so tiles do not
 //    re-read LDS.  The result (lane l: rows 4 (l / 16) .. +3, column l % 16
 //    of each 16-column group) holds both members of every rotation pair
-//    (column c and c + H/2) in one lane.
+//    (column c and c + H/2) in one lane.  B_Kh's columns are permuted as
+//    they are staged, so a lane's NP = H / 32 pairs are consecutive pair
+//    indices and their cos / sin are one 16-byte (H = 64: 8-byte) load of a
+//    table row: measured on MI355X (16 x 32 heads, 4096 tokens, rank 64),
+//    the per-pair 4-byte table loads cost about 7% of the kernel's time.
 //  * Rotation: pair (c, c + H/2) of row t turns by t theta_c.  Since
-//    <q, R(t) k> = <R(-t) q, k>, the lane turns its slice of q instead: to
-//    its first row's position with cos / sin from the caller's tables, then
-//    back by theta_c per following row (cos theta_c, sin theta_c are table
-//    row 1) -- four operations per pair and row instead of rotating the key
-//    and stepping the angle separately.
+//    <q, R(t) k> = <R(-t) q, k>, the lane turns its slice of q instead.  A
+//    lane's first result row in every tile sits at the same offset
+//    16 w + 4 (l / 16) from the tile's start, so q is turned back by that
+//    offset once per split; each tile then turns it back by the tile's own
+//    offset (one table row, the same for the whole wave), and by theta_c per
+//    following row (cos theta_c, sin theta_c are table row 1) -- four
+//    operations per pair and row instead of rotating the key and stepping
+//    the angle separately.  Measured on MI355X, a table row per row quad
+//    (2 KB of cos / sin per 4 KB tile) cost about 8% of the kernel's time.
 //  * Scores: the lane's key columns times the turned q (sigma log2 e folded
 //    in), summed over the 16 lanes of a DPP row; each lane then takes the
 //    score of its own A-operand row with one shuffle per row slot.
@@ -51,8 +59,34 @@ union R16 {
     bf16x8 b;
 };
 
+// Key column carried by column group j (of 16) and result lane rr.  Columns
+// are permuted so that the NP pairs a lane owns are consecutive pair indices
+// NP rr .. NP rr + NP - 1: its cos / sin then come from one vector load of a
+// table row.  Group p < NP holds the first member of pair NP rr + p, group
+// p + NP the second (column + H / 2), so both members stay in one lane.
+template <int H>
+__device__ __forceinline__ constexpr int rope_key_col(int j, int rr) {
+    constexpr int NP = H / 32;
+    return (j / NP) * (H / 2) + NP * rr + (j % NP);
+}
+
+template <int NP>
+__device__ __forceinline__ void load_pairs(const float* p, float* v) {
+    if constexpr (NP == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(p);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+        static_assert(NP == 2, "H is 64 or 128");
+        const float2 x = *reinterpret_cast<const float2*>(p);
+        v[0] = x.x; v[1] = x.y;
+    }
+}
+
 template <int H, int R>
 __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const float* rcos, const float* rsin) {
+    // Tiles in flight per wave (measured on MI355X: 3 or 4 were no faster on
+    // the 16 x 32-head, 4096-token rank-64 decode).
+    constexpr int D = 2;
     constexpr int NW = 4;
     constexpr int NJ = H / 16;     // 16-column groups of a key row
     constexpr int NP = H / 32;     // groups holding the first member of each pair
@@ -107,10 +141,15 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
     }
     float c1[NP], s1[NP];  // cos / sin of theta_c, c = 16 p + rr (table row 1)
     const int row1 = (a.L_cap > 1) ? HH : 0;  // a one-row table: row 0 (angle 0)
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        c1[p] = rcos[row1 + 16 * p + rr];
-        s1[p] = rsin[row1 + 16 * p + rr];
+    load_pairs<NP>(rcos + row1 + NP * rr, c1);
+    load_pairs<NP>(rsin + row1 + NP * rr, s1);
+    // cos / sin of the lane's first result row inside a tile, 16 wave + 4 g
+    // (a row past the table belongs to no token, so any angle serves there)
+    float cw[NP], sw[NP];
+    {
+        const int rw = min(TR * wave + 4 * g, a.L_cap - 1) * HH;
+        load_pairs<NP>(rcos + rw + NP * rr, cw);
+        load_pairs<NP>(rsin + rw + NP * rr, sw);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -129,9 +168,10 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
         const uint16_t* kbase = static_cast<const uint16_t*>(a.C_K) + (bh * a.L_cap + t0) * R + 8 * g;
         const uint16_t* vbase = static_cast<const uint16_t*>(a.C_V) + (bh * a.L_cap + t0) * R + 8 * g;
 
-        R16 kA[KS], vA[KS], kB[KS], vB[KS];
-        float cA[NP], sA[NP], cB[NP], sB[NP];
+        R16 kb[D][KS], vb[D][KS];
+        float cb[D][NP], sb[D][NP];
 
+        const int tb0 = wave * TR;
         auto load_tile = [&](int tb, R16* kr, R16* vr, float* cr, float* sr) {
             const int row = min(tb + rr, ntok - 1);
 #pragma unroll
@@ -139,20 +179,16 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
                 kr[ks].u = load16_stream(kbase + (size_t)row * R + 32 * ks);
                 vr[ks].u = load16_stream(vbase + (size_t)row * R + 32 * ks);
             }
-            const int ta = min(t0 + tb + 4 * g, a.L_cap - 1);  // position of the lane's first result row
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                cr[p] = rcos[(size_t)ta * HH + 16 * p + rr];
-                sr[p] = rsin[(size_t)ta * HH + 16 * p + rr];
-            }
+            const int ta = min(t0 + tb - tb0, a.L_cap - 1);  // the tile's offset in the split; see qv
+            load_pairs<NP>(rcos + (size_t)ta * HH + NP * rr, cr);
+            load_pairs<NP>(rsin + (size_t)ta * HH + NP * rr, sr);
         };
 
         // Both tiles are requested unconditionally (a wave with fewer rows
         // re-reads the split's last row): with a branch around them the waits
         // for the factors below would also wait for the tiles.
-        const int tb0 = wave * TR;
-        load_tile(tb0, kA, vA, cA, sA);
-        load_tile(tb0 + STEP, kB, vB, cB, sB);
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_tile(tb0 + d * STEP, kb[d], vb[d], cb[d], sb[d]);
 
 #pragma unroll
         for (int kk = 0; kk < NBT; ++kk) {
@@ -160,7 +196,13 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
             const int k = c / (H / 8);
             const int n0 = (c % (H / 8)) * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sBkT[(n0 + e) * BP + k] = uint16_t(bkr[kk][e >> 1] >> ((e & 1) * 16));
+            for (int e = 0; e < 8; ++e) {
+                // key column n0 + e sits in column group j, lane rr' (see rope_key_col)
+                const int col = n0 + e;
+                const int hi = col / HH, ch = col % HH;
+                const int nn = 16 * ((ch % NP) + NP * hi) + ch / NP;
+                sBkT[nn * BP + k] = uint16_t(bkr[kk][e >> 1] >> ((e & 1) * 16));
+            }
             sh_bv[c] = bvr[kk];
         }
         sh_q[tid] = q_word_value(q_word, a.q_dt, q_idx);
@@ -168,7 +210,16 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 
         float qv[NJ];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) qv[j] = sh_q[16 * j + rr] * a.scale_log2;
+        for (int j = 0; j < NJ; ++j) qv[j] = sh_q[rope_key_col<H>(j, rr)] * a.scale_log2;
+        // q turned back once by the lane's fixed row offset in a tile: each tile
+        // then needs the angle of its offset in the split only -- one table row
+        // for the whole wave instead of one per row quad.
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const float x = qv[p], y = qv[p + NP];
+            qv[p] = fmaf(x, cw[p], y * sw[p]);
+            qv[p + NP] = fmaf(y, cw[p], -(x * sw[p]));
+        }
 
         R16 breg[NJ * KS];  // this lane's B operand fragments of B_Kh
 #pragma unroll
@@ -251,19 +302,22 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 
         const int nt = (ntok > tb0) ? (ntok - tb0 + STEP - 1) / STEP : 0;
         int k = 0;
-        for (; k + 3 < nt; k += 2) {
-            consume(tb0 + k * STEP, kA, vA, cA, sA);
-            load_tile(tb0 + (k + 2) * STEP, kA, vA, cA, sA);
-            __builtin_amdgcn_sched_barrier(0);
-            consume(tb0 + (k + 1) * STEP, kB, vB, cB, sB);
-            load_tile(tb0 + (k + 3) * STEP, kB, vB, cB, sB);
-            __builtin_amdgcn_sched_barrier(0);
+        for (; k + 2 * D - 1 < nt; k += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                consume(tb0 + (k + d) * STEP, kb[d], vb[d], cb[d], sb[d]);
+                load_tile(tb0 + (k + d + D) * STEP, kb[d], vb[d], cb[d], sb[d]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        const int rem = nt - k;
-        if (rem >= 1) consume(tb0 + k * STEP, kA, vA, cA, sA);
-        if (rem >= 3) load_tile(tb0 + (k + 2) * STEP, kA, vA, cA, sA);
-        if (rem >= 2) consume(tb0 + (k + 1) * STEP, kB, vB, cB, sB);
-        if (rem >= 3) consume(tb0 + (k + 2) * STEP, kA, vA, cA, sA);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (k + d < nt) consume(tb0 + (k + d) * STEP, kb[d], vb[d], cb[d], sb[d]);
+            if (k + d + D < nt) load_tile(tb0 + (k + d + D) * STEP, kb[d], vb[d], cb[d], sb[d]);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (k + D + d < nt) consume(tb0 + (k + D + d) * STEP, kb[d], vb[d], cb[d], sb[d]);
 
         // ---- merge the wave's rows (lanes of one DPP row hold different rows) --
         const float Mw = wave_max(m);
