@@ -24,7 +24,9 @@
 //    and bumps the tile's arrival counter; the block that arrives last sums
 //    the KS partials (exact in any order), resets the counter, applies the
 //    scales, rounds once to the cache dtype and writes row pos[b] of every
-//    head's K and V cache.
+//    head's K and V cache.  The hand-off relies on the same gfx950 ordering
+//    as the decode merge (split_merge.hpp): write-through device-scope
+//    stores acknowledged before a relaxed device-scope counter increment.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
 

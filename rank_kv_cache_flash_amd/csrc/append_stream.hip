@@ -35,7 +35,10 @@
 //    KS > 1 each block stores its sum write-through and takes a ticket; the
 //    last of the KS blocks of a tile adds the others' sums in slice order
 //    (own slice from registers), so the result does not depend on which
-//    block finished last, resets the counter and writes the rows.
+//    block finished last, resets the counter and writes the rows.  The
+//    hand-off relies on the same gfx950 ordering as the decode merge
+//    (split_merge.hpp): write-through device-scope stores acknowledged
+//    before a relaxed device-scope ticket.
 //  * Rows are rounded once to the cache dtype; int8 caches store absmax
 //    codes with an fp16 scale per (row, head) (max over the head's lanes by
 //    DPP).

@@ -11,6 +11,20 @@
 // served from a stale L2 line), merges them in split order (so the result
 // does not depend on which split finished last), writes out[b, h, :] and
 // resets the counter.  No cache-wide writeback or invalidate is needed.
+//
+// Ordering assumption.  The partials and the counter are all relaxed
+// device-scope atomics, so the language memory model alone does not order
+// the partial stores before the increment.  The order comes from gfx950
+// itself: a device-scope store is written through to memory (it does not
+// stay in this XCD's L2), the s_waitcnt(0) below returns only once every
+// such store of the wave has been acknowledged, and the barrier then holds
+// the increment back until all waves got there; the reader's device-scope
+// loads bypass the non-coherent L2 copies.  The portable form -- a release
+// increment and an acquire on the last split -- compiles to a full L2
+// writeback before the increment and an L2 invalidate after it; measured on
+// MI355X it made the 1 x 32-head, 1088-token step 1.2 us slower (6.87 ->
+// 8.10 us), so it is not used.  The cross-XCD repeated-merge test guards
+// this assumption.
 #pragma once
 
 #include "wsvd_common.hpp"
