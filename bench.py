@@ -531,10 +531,10 @@ def cpu_baseline(w, gpu_out, budget_s=12.0):
 
 
 # ---------------------------------------------------------------------------
-def launch_floors(blocks, nbytes, steps, warmup):
-    """What a launch on the decode's grid cannot beat on this device, timed
-    like the step: an empty kernel, and a stream of the same bytes with every
-    request issued at once (wsvd_floor_probe), rotating copies over >= 1 GiB."""
+def launch_floors(blocks, nbytes, steps, warmup, decode_grid):
+    """What a launch of this size cannot beat on this device, timed like the
+    step: an empty kernel, and a stream of the same bytes with every request
+    issued at once (wsvd_floor_probe), rotating copies over >= 1 GiB."""
     import torch
     from rank_kv_cache_flash_amd import wsvd
     sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
@@ -543,10 +543,13 @@ def launch_floors(blocks, nbytes, steps, warmup):
     t_empty = graph_time(lambda i: wsvd.floor_probe(0, blocks, sink), steps, warmup)
     t_stream = graph_time(lambda i: wsvd.floor_probe(1, blocks, sink, srcs[i % copies]), steps, warmup, copies)
     del srcs
-    return {"grid_blocks": blocks, "bytes": int(nbytes), "empty_launch_us": round(t_empty * 1e6, 3),
+    return {"grid_blocks": blocks, "decode_grid_blocks": decode_grid, "bytes": int(nbytes),
+            "empty_launch_us": round(t_empty * 1e6, 3),
             "stream_us": round(t_stream * 1e6, 3), "stream_GB_per_s": round(nbytes / t_stream / 1e9, 1),
-            "note": "wsvd_floor_probe on the decode's grid: empty kernel, and the same bytes streamed with all "
-                    "requests issued at once; graph replay, cold HBM"}
+            "stream_pct_of_hbm_peak": round(100.0 * nbytes / t_stream / 1e9 / HBM_PEAK_GBS, 1),
+            "note": "wsvd_floor_probe: an empty kernel, and the decode kernel's bytes streamed with every request "
+                    "issued at once (<= 64 KB per block: the decode's grid, or the smallest multiple of it that "
+                    "fits); graph replay, cold HBM"}
 
 
 def measure(cfg, steps, warmup, n_splits=None, cpu_budget=None, extras=True):
@@ -585,10 +588,13 @@ def measure(cfg, steps, warmup, n_splits=None, cpu_budget=None, extras=True):
         "warm_cache": {"us_per_step": round(tw * 1e6, 3), "GB_per_s": round(w.step_bytes / tw / 1e9, 1),
                        "note": "every step on one input copy (cache-resident where it fits); not an HBM figure"},
     }
-    blocks = cfg.nb * cfg.nh * w.S
+    # The probe streams at most 4096 16-byte chunks per block: larger steps
+    # use the smallest multiple of the decode's grid that fits.
+    grid = cfg.nb * cfg.nh * w.S
+    blocks = grid * max(1, math.ceil(w.decode_kernel_bytes / (16 * grid) / 4096))
     fb = w.decode_kernel_bytes // (16 * blocks) * 16 * blocks
-    if 0 < fb // (16 * blocks) <= 4096:
-        rec["floors"] = launch_floors(blocks, fb, steps, warmup)
+    if fb > 0 and blocks <= (1 << 20):
+        rec["floors"] = launch_floors(blocks, fb, steps, warmup, grid)
     if cpu_budget:
         torch.cuda.synchronize()
         rec["cpu_baseline"], rec["parity_max_rel_err_vs_oracle"] = cpu_baseline(w, w.out, budget_s=cpu_budget)
