@@ -635,6 +635,8 @@ def main():
                     help="decode-loop / step-loop / copy-calib / counters: plain launch loops for traces and counters")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads for --mode counters")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--graph", action="store_true",
+                    help="decode-loop / step-loop / rope-loop: replay the calls as the benchmark does (a HIP graph)")
     ap.add_argument("--no-shared", dest="shared", action="store_false",
                     help="skip the shared-latent (conventional factorisation) ablation")
     ap.add_argument("--no-factorize", dest="factorize", action="store_false",
@@ -715,8 +717,11 @@ def main():
             ws = wsvd.decode_workspace(cfg.nb, cfg.nh, cfg.H, cfg.L_cap, 0)
             calls.append(wsvd.PreparedDecodeRope(d["q"], d["C_K"], d["C_V"], d["B_K"], d["B_V"], d["L"], c, s_,
                                                  workspace=ws, out=out))
-        for i in range(args.steps):
-            calls[i % len(calls)]()
+        if args.graph:
+            graph_timing(lambda i: calls[i % len(calls)](), args.steps, 5, len(calls), regions=1)
+        else:
+            for i in range(args.steps):
+                calls[i % len(calls)]()
         torch.cuda.synchronize()
         print(json.dumps({"mode": args.mode, "workload": cfg.name, "launches": args.steps}))
         return
@@ -782,13 +787,17 @@ def main():
         print(json.dumps({"mode": args.mode, "shape": f"E={E} nh={nh} H={H} r={r}", "launches": args.steps}))
         return
     if args.mode in ("decode-loop", "step-loop"):
-        # Plain launch loops (no graph) for kernel traces: the split kernel
-        # alone (partials only, as timed for the roofline) or whole steps.
+        # Launch loops for kernel traces: the split kernel alone (partials
+        # only, as timed for the roofline) or whole steps.  Plain launches, or
+        # with --graph the benchmark's own graph replay of the same calls.
         cfg = CONFIGS[args.config]
         w = Workload(cfg, n_splits=args.splits or None)
         fn = w.decode_only if args.mode == "decode-loop" else w.step
-        for i in range(args.steps):
-            fn(i)
+        if args.graph:
+            graph_timing(fn, args.steps, 5, w.copies, regions=1)
+        else:
+            for i in range(args.steps):
+                fn(i)
         torch.cuda.synchronize()
         print(json.dumps({"mode": args.mode, "workload": cfg.name, "launches": args.steps,
                           "decode_kernel_bytes": w.decode_kernel_bytes, "splits": w.S}))
