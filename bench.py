@@ -645,7 +645,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "the benchmark measures one GPU; the multi-GPU split is not implemented (run with --gpus 1)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
