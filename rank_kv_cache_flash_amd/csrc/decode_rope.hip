@@ -12,18 +12,25 @@
 //
 // Per (b, h, split) workgroup of 4 waves; a wave takes 16-row tiles (tile
 // k of wave w starts at row 16 w + 64 k of the split), D = 2 tiles in flight.
+//  * Loads: each wave-wide 16-byte load reads whole latent rows, 1 KB
+//    contiguous (8 rows at rank 64).  The matrix-core operand wants a lane
+//    per row instead, so each tile is staged through the wave's own LDS
+//    buffer: stored row-wise with the 16-byte chunks of row t xor-swizzled by
+//    t % (chunks per row), which keeps the stores, the operand reads and the
+//    transposing reads below free of bank conflicts.  Loading the operand
+//    layout straight from the cache (half of each of 16 rows per load)
+//    measured about 20% slower on MI355X, with or without the arithmetic.
 //  * K tile: v_mfma_f32_16x16x32_bf16 with the 16 latent rows as the A
 //    operand (lane l: row l % 16, 8 consecutive ranks at 8 (l / 16)), read
-//    straight from the cache, and B_Kh as the B operand: staged transposed
-//    in LDS once, then each lane keeps its fragments of the whole factor in
+//    from the staged tile, and B_Kh as the B operand: staged transposed in
+//    LDS once, then each lane keeps its fragments of the whole factor in
 //    registers for the split (r H / 512 u32x4 per lane), so tiles do not
-//    re-read LDS.  The result (lane l: rows 4 (l / 16) .. +3, column l % 16
+//    re-read it.  The result (lane l: rows 4 (l / 16) .. +3, column l % 16
 //    of each 16-column group) holds both members of every rotation pair
 //    (column c and c + H/2) in one lane.  B_Kh's columns are permuted as
 //    they are staged, so a lane's NP = H / 32 pairs are consecutive pair
 //    indices and their cos / sin are one 16-byte (H = 64: 8-byte) load of a
-//    table row: measured on MI355X (16 x 32 heads, 4096 tokens, rank 64),
-//    the per-pair 4-byte table loads cost about 7% of the kernel's time.
+//    table row.
 //  * Rotation: pair (c, c + H/2) of row t turns by t theta_c.  Since
 //    <q, R(t) k> = <R(-t) q, k>, the lane turns its slice of q instead.  A
 //    lane's first result row in every tile sits at the same offset
@@ -35,11 +42,18 @@
 //    the angle separately.  Measured on MI355X, a table row per row quad
 //    (2 KB of cos / sin per 4 KB tile) cost about 8% of the kernel's time.
 //  * Scores: the lane's key columns times the turned q (sigma log2 e folded
-//    in), summed over the 16 lanes of a DPP row; each lane then takes the
-//    score of its own A-operand row with one shuffle per row slot.
-//  * Values stay in latent space: the lane accumulates p c_V of its row and
-//    rank chunk (online softmax per lane), and the split's r-vector is
-//    projected through B_Vh once, as in the folded kernel.
+//    in), summed over the 16 lanes of a DPP row: every lane of row quad
+//    l / 16 then holds the scores of tile rows 4 (l / 16) .. +3.
+//  * Values stay in latent space and go through the matrix cores:
+//    o += V^T p with v_mfma_f32_16x16x16_bf16, where the A operand (rank
+//    l % 16, rows 4 (l / 16) ..) comes from the staged value tile through
+//    gfx950's transposing LDS read and the B operand is the lane's own four
+//    weights -- exactly the rows whose scores it holds, so no shuffle is
+//    needed.  The weights are rounded once to bf16 and the softmax sum counts
+//    them as rounded.  One running max serves the whole wave (an MFMA sums
+//    rows of all four row quads), moved only when a score passes it by 2^8.
+//    The split's r-vector is projected through B_Vh once, as in the folded
+//    kernel.
 //  * Prologue: q, both factors and the cos / sin of one position step are
 //    requested first, then the wave's first two tiles without a branch, so
 //    staging B_Kh into LDS overlaps the tiles' flight.
@@ -52,7 +66,18 @@
 namespace wsvd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define WSVD_LDS_AS __attribute__((address_space(3)))
+
+// gfx950's transposing LDS read: in each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8,
+// i/4+12 -- so when those 16 lanes address 4 rows x 16 columns of a row-major
+// bf16 tile, lane i holds the 4 rows of column i.
+__device__ __forceinline__ bf16x4 tr_read_b64(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((WSVD_LDS_AS bf16x4*)(WSVD_LDS_AS unsigned char*)p);
+}
 
 union R16 {
     u32x4 u;
@@ -100,6 +125,12 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
     constexpr int HH = H / 2;
 
     __shared__ __attribute__((aligned(16))) uint16_t sBkT[H * BP];
+    constexpr int NG = R / 16;            // 16-rank groups of the value product
+    constexpr int RB = 2 * R;             // bytes per latent row
+    constexpr int CPR = R / 8;            // 16-byte chunks per latent row
+    constexpr int RPI = 64 / CPR;         // rows per wave-wide 16-byte load (1 KB, contiguous)
+    static_assert(RPI * KS == TR, "a tile is KS contiguous loads per cache");
+    __shared__ __attribute__((aligned(16))) unsigned char sKV[NW * 2 * TR * RB];
     __shared__ u32x4 sh_bv[NBC];
     __shared__ float sh_q[256];  // q in [0, H); every thread stores its value
     __shared__ float sh_red_o[NW][R];
@@ -165,19 +196,21 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 
     if (ntok > 0) {  // uniform over the block
         // ---- first two tiles of the wave, then q and the factors staged ------------
-        const uint16_t* kbase = static_cast<const uint16_t*>(a.C_K) + (bh * a.L_cap + t0) * R + 8 * g;
-        const uint16_t* vbase = static_cast<const uint16_t*>(a.C_V) + (bh * a.L_cap + t0) * R + 8 * g;
+        const uint16_t* kbase = static_cast<const uint16_t*>(a.C_K) + (bh * a.L_cap + t0) * R + 8 * (lane % CPR);
+        const uint16_t* vbase = static_cast<const uint16_t*>(a.C_V) + (bh * a.L_cap + t0) * R + 8 * (lane % CPR);
 
         R16 kb[D][KS], vb[D][KS];
         float cb[D][NP], sb[D][NP];
 
         const int tb0 = wave * TR;
         auto load_tile = [&](int tb, R16* kr, R16* vr, float* cr, float* sr) {
-            const int row = min(tb + rr, ntok - 1);
+            // Load ks covers tile rows RPI ks .. RPI ks + RPI - 1 whole (lane: row
+            // lane / CPR, chunk lane % CPR): every wave load is 1 KB contiguous.
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                kr[ks].u = load16_stream(kbase + (size_t)row * R + 32 * ks);
-                vr[ks].u = load16_stream(vbase + (size_t)row * R + 32 * ks);
+                const int row = min(tb + RPI * ks + lane / CPR, ntok - 1);
+                kr[ks].u = load16_stream(kbase + (size_t)row * R);
+                vr[ks].u = load16_stream(vbase + (size_t)row * R);
             }
             const int ta = min(t0 + tb - tb0, a.L_cap - 1);  // the tile's offset in the split; see qv
             load_pairs<NP>(rcos + (size_t)ta * HH + NP * rr, cr);
@@ -227,12 +260,39 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 breg[ks * NJ + j].u = *reinterpret_cast<const u32x4*>(&sBkT[(16 * j + rr) * BP + 32 * ks + 8 * g]);
+        // m is shared by the whole wave: one value-product MFMA sums rows of all
+        // four row quads, so their weights need one reference.
         float m = kNegInf, l = 0.f;
-        float acc[8 * KS];
+        f32x4 oacc[NG];
 #pragma unroll
-        for (int c = 0; c < 8 * KS; ++c) acc[c] = 0.f;
+        for (int j = 0; j < NG; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // The wave's tile in LDS, swizzled: 16-byte chunk c of row t sits at
+        // t RB + 16 (c ^ (t % CPR)), so the row-wise stores, the operand reads
+        // (16 rows, one chunk) and the transposing reads are free of bank conflicts.
+        unsigned char* sKw = sKV + wave * 2 * TR * RB;
+        unsigned char* sVw = sKw + TR * RB;
+        auto swz = [](int t, int c) { return t * RB + 16 * (c ^ (t % CPR)); };
+        int woff[KS], koff[KS], voff[NG];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            woff[ks] = swz(RPI * ks + lane / CPR, lane % CPR);
+            koff[ks] = swz(rr, g + 4 * ks);  // A operand: row rr, ranks 8 g + 32 ks ..
+        }
+#pragma unroll
+        for (int j = 0; j < NG; ++j)  // transposing read: rows 4 g + rr / 4, 8-byte chunk rr % 4 of rank group j
+            voff[j] = swz(4 * g + (rr >> 2), 2 * j + ((rr & 3) >> 1)) + 8 * (rr & 1);
 
         auto consume = [&](int tb, const R16* kr, const R16* vr, const float* cr, const float* sr) {
+            // Stage the tile in LDS and read the key tile back in the matrix-core
+            // operand layout (lane: row rr, 8 ranks at 8 g + 32 ks).
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                *reinterpret_cast<u32x4*>(sKw + woff[ks]) = kr[ks].u;
+                *reinterpret_cast<u32x4*>(sVw + woff[ks]) = vr[ks].u;
+            }
+            R16 ka[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ka[ks].u = *reinterpret_cast<const u32x4*>(sKw + koff[ks]);
             f32x4 kt[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) kt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -242,7 +302,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
                 for (int j = 0; j < NJ; ++j) {
                     R16 bf;
                     bf = breg[ks * NJ + j];
-                    kt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks].b, bf.b, kt[j], 0, 0, 0);
+                    kt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks].b, bf.b, kt[j], 0, 0, 0);
                 }
             }
             // rows 4 g + i sit at positions t0 + tb + 4 g + i: q turned back
@@ -270,34 +330,34 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
                 d = group_sum<16>(d);
                 sc[i] = (tb + 4 * g + i < ntok) ? d : kNegInf;
             }
-            // the score of this lane's own row (A-operand row rr lives in quad rr / 4)
-            const int src = 16 * (rr >> 2);
-            const float y0 = __shfl(sc[0], src, 64), y1 = __shfl(sc[1], src, 64);
-            const float y2 = __shfl(sc[2], src, 64), y3 = __shfl(sc[3], src, 64);
-            const int q4 = rr & 3;
-            const float my = q4 == 0 ? y0 : (q4 == 1 ? y1 : (q4 == 2 ? y2 : y3));
-            // The running max moves only when some lane's score grows past it by
-            // more than 2^8 (or is first set): below that, exp2(score - m) stays
-            // under 256 and the accumulators need no rescaling.
-            if (__builtin_amdgcn_ballot_w64(my > m + 8.f)) {
-                const float mn = (my > m + 8.f) ? my : m;
+            // The running max moves only when some score grows past it by more
+            // than 2^8 (or is first set): below that, exp2(score - m) stays under
+            // 256 and the accumulators need no rescaling.
+            const float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f)) {
+                const float mn = fmaxf(m, wave_max(mloc));
                 const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
                 l *= alpha;
 #pragma unroll
-                for (int c = 0; c < 8 * KS; ++c) acc[c] *= alpha;
+                for (int j = 0; j < NG; ++j) oacc[j] *= alpha;
                 m = mn;
             }
-            const float pr = fast_exp2(my - ((m == kNegInf) ? 0.f : m));
-            l += pr;
+            const float mu = (m == kNegInf) ? 0.f : m;
+            // Weights of this lane's rows 4 g .. 4 g + 3, rounded once to bf16 and
+            // counted in l as rounded, so the numerator and the denominator use the
+            // same weights: the B operand of the value product (every column alike).
+            f32x4 pw;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int i = 0; i < 4; ++i) pw[i] = fast_exp2(sc[i] - mu);
+            const bf16x4 pb = __builtin_convertvector(pw, bf16x4);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const uint32_t w = vr[ks].u[c >> 1];
-                    const float vc = (c & 1) ? bf16_hi(w) : bf16_lo(w);
-                    acc[8 * ks + c] = fmaf(pr, vc, acc[8 * ks + c]);
-                }
-            }
+            for (int i = 0; i < 4; ++i) l += (float)pb[i];
+            // o += V^T p on matrix cores: the A operand (rank l % 16, rows 4 g ..)
+            // comes from the transposing LDS read of the tile just stored.
+#pragma unroll
+            for (int j = 0; j < NG; ++j)
+                oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, tr_read_b64(sVw + voff[j])),
+                                                                     __builtin_bit_cast(s16x4, pb), oacc[j], 0, 0, 0);
         };
 
         const int nt = (ntok > tb0) ? (ntok - tb0 + STEP - 1) / STEP : 0;
@@ -319,20 +379,18 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
         for (int d = 0; d < D; ++d)
             if (k + D + d < nt) consume(tb0 + (k + D + d) * STEP, kb[d], vb[d], cb[d], sb[d]);
 
-        // ---- merge the wave's rows (lanes of one DPP row hold different rows) --
-        const float Mw = wave_max(m);
-        const float f = (m == kNegInf) ? 0.f : fast_exp2(m - Mw);
-        l = group_sum<16>(l * f);
-#pragma unroll
-        for (int c = 0; c < 8 * KS; ++c) acc[c] = group_sum<16>(acc[c] * f);
+        // ---- merge the wave's row quads (one running max for the wave) ---------
+        // l: every lane of a DPP row holds its quad's sum; oacc: lane 16 g holds
+        // ranks 16 j + 4 g .. + 3 (the MFMA already summed over all 16 rows).
+        l = sum_over_slots<16>(l);
         if (rr == 0) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int j = 0; j < NG; ++j)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) sh_red_o[wave][32 * ks + 8 * g + c] = acc[8 * ks + c];
+                for (int i = 0; i < 4; ++i) sh_red_o[wave][16 * j + 4 * g + i] = oacc[j][i];
         }
         if (lane == 0) {
-            sh_red_m[wave] = Mw;
+            sh_red_m[wave] = m;
             sh_red_l[wave] = l;
         }
         __syncthreads();
