@@ -120,6 +120,7 @@ class Workload:
 
 MIN_REGION_S = 1e-3      # every timed region lasts at least this long
 REGIONS = 5              # timed regions per measurement; the median is reported
+WARM_S = 0.2             # untimed replays first, until the graph has run this long
 
 
 def graph_timing(fn, steps, warmup, copies=1, min_region_s=MIN_REGION_S, regions=REGIONS):
@@ -128,10 +129,14 @@ def graph_timing(fn, steps, warmup, copies=1, min_region_s=MIN_REGION_S, regions
     The graph holds n calls, n = `steps` rounded up to a multiple of
     `copies`, so one replay touches every input copy (callers size `copies`
     so that is >= 1 GiB) whatever `steps` is.  After `warmup` eager calls and
-    one untimed replay, each timed region is k back-to-back replays between
-    two events on the replay stream (k chosen so a region lasts >=
-    min_region_s), bracketed by device synchronisation; the median over
-    `regions` regions is returned with every region's figure."""
+    untimed replays for at least WARM_S of GPU time (the clocks of a
+    compute-heavier kernel ramp up over tens of ms of sustained load: the
+    rotary-key decode's first replays run 20 % slower than its steady state,
+    while the memory-bound split kernel is flat), each timed region is k
+    back-to-back replays between two events on the replay stream (k chosen so
+    a region lasts >= min_region_s), bracketed by device synchronisation;
+    the median over `regions` regions is returned with every region's
+    figure."""
     import torch
     n = max(1, -(-max(steps, copies) // copies) * copies)
     s = torch.cuda.Stream()
@@ -147,6 +152,10 @@ def graph_timing(fn, steps, warmup, copies=1, min_region_s=MIN_REGION_S, regions
             fn(i)
     g.replay()
     torch.cuda.synchronize()
+    t_warm = time.time() + WARM_S
+    while time.time() < t_warm:
+        g.replay()
+        torch.cuda.synchronize()
 
     def region(k):
         e0 = torch.cuda.Event(enable_timing=True)
