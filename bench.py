@@ -12,7 +12,8 @@ Inputs are resident in HBM before timing starts.
 Timing: the steps are captured once into a HIP graph holding K steps (at
 least one per input copy, and enough copies that one replay reads >= 1 GiB
 of distinct inputs, so every step reads cold HBM rather than the 256 MB
-Infinity Cache).  After W eager warm-up steps and one untimed replay, each
+Infinity Cache).  After W eager warm-up steps, the graph is replayed untimed
+for >= 200 ms (the GPU's clocks ramp up under sustained load); then each
 timed region is one or more back-to-back replays (>= 1 ms) between events on
 the replay stream, bracketed by device synchronisation; the median over five
 regions is reported with every region's figure.
