@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(DecodeArgs a, const fl
         bkr[k] = bkc[tid + 256 * k];
         bvr[k] = bvc[tid + 256 * k];
     }
-    float c1[NP], s1[NP];  // cos / sin of theta_c, c = 16 p + rr (table row 1)
+    float c1[NP], s1[NP];  // cos / sin of theta_c for the lane's pairs c = NP rr + p (table row 1)
     const int row1 = (a.L_cap > 1) ? HH : 0;  // a one-row table: row 0 (angle 0)
     load_pairs<NP>(rcos + row1 + NP * rr, c1);
     load_pairs<NP>(rsin + row1 + NP * rr, s1);
