@@ -615,6 +615,28 @@ def test_large_grid_merges_in_second_launch(W):
     check("small grid S=4", f64(out8), O.decode_attn(small), TOL["bf16"])
 
 
+@pytest.mark.parametrize("nb", [2, 64, 65, 200, 256, 257])
+def test_large_grid_ragged_many_sequences(W, nb):
+    """Grids of 2048 blocks or more over 2..257 sequences (so from 256 heads
+    down to 2): ragged lengths with ties, empty sequences and lengths past
+    L_cap, a NaN-poisoned workspace (a partial left unwritten would show), and
+    the whole output against the oracle."""
+    S = 4
+    nh = -(-2048 // (S * nb))
+    L_cap = 64
+    rng = np.random.default_rng(5000 + nb)
+    L = rng.integers(0, L_cap + 1, nb).astype(np.int32)
+    L[rng.integers(0, nb, max(1, nb // 8))] = 0
+    L[rng.integers(0, nb, max(1, nb // 8))] = L_cap + 40
+    assert nb * nh * S >= 2048
+    inp = I.make_decode_inputs(nb, nh, 64, 16, L, L_cap, seed=5100 + nb, act_dt="bf16", C_dt="bf16",
+                               fill=np.minimum(L, L_cap), q_gain=2.0 * 64)
+    out, _, _ = run_decode(W, inp, n_splits=S, poison=True)
+    g = f64(out)
+    check(f"large grid nb={nb} nh={nh}", g, O.decode_attn(inp), TOL["bf16"])
+    assert not g[L == 0].any(), "L = 0 must give zero rows"
+
+
 def test_dense_baseline_large_grid(W):
     """2048 split blocks: the dense baseline also merges in a second launch."""
     L = (np.arange(64, dtype=np.int32) * 37) % 300 + 1

@@ -94,3 +94,20 @@ def test_rope_decode_large_grid(W):
     inp = I.make_decode_inputs(64, 8, 64, 32, L, 300, seed=1600, act_dt="bf16", C_dt="bf16", q_gain=4.0 * 64)
     g, _ = run(W, inp, n_splits=4)
     assert rel(g, O.decode_attn_rope(inp)) <= TOL
+
+
+@pytest.mark.parametrize("nb", [64, 65])
+def test_rope_decode_large_grid_ragged(W, nb):
+    """2048+ blocks over ragged lengths with ties and an empty sequence
+    (partials merged in a second launch)."""
+    rng = np.random.default_rng(1700 + nb)
+    L = rng.integers(1, 301, nb).astype(np.int32)
+    L[::7] = L[0]
+    L[3] = 0
+    inp = I.make_decode_inputs(nb, 8, 64, 32, L, 300, seed=1700 + nb, act_dt="bf16", C_dt="bf16",
+                               q_gain=4.0 * 64)
+    g, _ = run(W, inp, n_splits=4)
+    e = rel(g, O.decode_attn_rope(inp))
+    print(f"[parity] rope large grid nb={nb}: max|err|/max|ref| = {e:.3e}", flush=True)
+    assert e <= TOL
+    assert np.all(g[3] == 0)
