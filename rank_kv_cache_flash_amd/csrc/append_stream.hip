@@ -12,12 +12,16 @@
 // Block = 8 waves; output tile = 64 rows of x  x  64 columns of one factor
 // (128-byte rows of A); E is cut into KS slices, the fewest (halving) that
 // give about 160+ blocks: 4 slices and 192 blocks at the LLaVA-7B step shape.
-//  * Stage = 256 rows of A (64 columns) and the matching 256 k of x.  Each
-//    wave owns a 32-k slice of every stage and computes all 64 x 64 outputs
-//    for it, so each byte of A and of x is read from LDS once per block.  x
-//    is loaded as whole 512-byte row pieces and staged in LDS beside A
-//    (reading the operand layout straight from memory, 16 rows x 64 bytes
-//    per load, measured 1.2 us slower at the LLaVA-7B step shape).
+//  * Stage = 256 rows of A (64 columns) and the matching 256 k of x.  The
+//    8 waves are 4 k-groups x 2 column halves: a wave owns a 64-k slice of
+//    every stage and the 64 x 32 outputs of its half, so each byte of A is
+//    read from LDS once per block and each byte of x twice.  (8 k-groups of
+//    32 k, every wave computing all 64 x 64 outputs, read x once but sum
+//    twice as many partial tiles at the end: 0.44 us slower at the LLaVA-7B
+//    step shape; 2 k-groups x 4 column quarters, reading x four times, as
+//    slow as 8.)  x is loaded as whole 512-byte row pieces and staged in LDS
+//    beside A (reading the operand layout straight from memory, 16 rows x
+//    64 bytes per load, measured 1.2 us slower at the LLaVA-7B step shape).
 //  * A arrives n-contiguous; its stage is stored to LDS row-major (rows
 //    padded so the reads below are free of bank conflicts) and the B
 //    operands are read with gfx950's transposing LDS read
@@ -31,7 +35,7 @@
 //    right after consuming stage s, with no branch around the request.
 //  * Blocks are placed so that each XCD runs one E slice (its L2 then holds
 //    a quarter of x).
-//  * The 8 waves' partial tiles are summed in LDS in wave order; each thread
+//  * The 4 k-groups' partial tiles are summed in LDS in k order; each thread
 //    then owns 8 consecutive outputs of one row, i.e. of one head.  With
 //    KS > 1 each block stores its sum write-through and takes a ticket; the
 //    last of the KS blocks of a tile adds the others' sums in slice order
@@ -44,9 +48,10 @@
 //    codes with an fp16 scale per (row, head) (max over the head's lanes by
 //    DPP).
 // Where the time goes (MI355X, 64 x 4096 -> 2 x 1536, timing copies with
-// parts removed): launch 1.8 us, result stores 1.5, the stage loop 1.5,
-// the 8-wave sum 1.9, the split-E exchange 3.7 (three dependent device-
-// scope round trips), and about 5 us of loads on top.
+// parts removed, taken with 8 k-groups): launch 1.8 us, result stores 1.5,
+// the stage loop 1.5, the sum across waves 1.9 (0.44 us less with the 4
+// k-groups above), the split-E exchange 3.7 (three dependent device-scope
+// round trips), and about 5 us of loads on top.
 #include "wsvd_common.hpp"
 #include "wsvd_internal.hpp"
 
@@ -61,6 +66,9 @@ typedef float as_f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStageK = 256;   // rows of A per stage
 constexpr int kWaves = 8;
+constexpr int kKGroups = 4;                   // waves = k-groups x column groups
+constexpr int kCGroups = kWaves / kKGroups;
+constexpr int kKSteps = kStageK / 32 / kKGroups;  // 32-k MFMA steps per wave per stage
 constexpr int kDepth = 4;      // stages in flight (registers)
 constexpr int kRows = 64;      // rows of x per block
 constexpr int kTargetBlocks = 160;
@@ -77,7 +85,7 @@ struct Tile {
     static constexpr int XSTAGE_BYTES = kRows * XPITCH;
     static constexpr int BUF_BYTES = STAGE_BYTES + XSTAGE_BYTES;  // one stage of A and x
     static constexpr int RED_PITCH = NT + 4;                 // floats per reduction row (bank spread)
-    static constexpr int RED_BYTES = kWaves * kRows * RED_PITCH * 4;
+    static constexpr int RED_BYTES = kKGroups * kRows * RED_PITCH * 4;
     static constexpr int LDS_BYTES = (2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES;
 };
 
@@ -181,14 +189,16 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
     // at the LLaVA-7B step shape).  Rows past nb start past the end of x, where
     // buffer loads return zeros.  The stage goes to LDS (padded rows) and each
     // wave reads back its fragments of 16-row group t: row 16 t + lane % 16,
-    // k = the wave's 32-k slice, 8 (lane / 16) onwards.
+    // k = the start of the wave's k-group slice (+ 32 per MFMA step),
+    // 8 (lane / 16) onwards.
     uint32_t x_voff[4], x_lds[4], x_frag[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = tid + 512 * i;
         x_voff[i] = ((uint32_t)(m0 + c / 32) * (uint32_t)a.E + (uint32_t)(e_beg + 8 * (c % 32))) * 2u;
         x_lds[i] = (uint32_t)(T::STAGE_BYTES + (c / 32) * T::XPITCH + (c % 32) * 16);
-        x_frag[i] = (uint32_t)(T::STAGE_BYTES + (16 * i + (lane & 15)) * T::XPITCH + 64 * wave + 16 * (lane >> 4));
+        x_frag[i] = (uint32_t)(T::STAGE_BYTES + (16 * i + (lane & 15)) * T::XPITCH + 64 * kKSteps * (wave / kCGroups) +
+                               16 * (lane >> 4));
     }
 
     u32x4 ar[kDepth][T::NA], xr[kDepth][4];
@@ -201,16 +211,18 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
             xr[d][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_voff[t], s * kStageK * 2, 0);
     };
 
-    as_f32x4 acc[4][T::NJ];
+    constexpr int NJW = T::NJ / kCGroups;  // 16-column groups of the wave's columns
+    as_f32x4 acc[4][NJW];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < T::NJ; ++j) acc[t][j] = as_f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJW; ++j) acc[t][j] = as_f32x4{0.f, 0.f, 0.f, 0.f};
 
     // B operand addresses inside a stage: lane s of each 16-lane group points
-    // at row (its group's 8-k block) + s / 4 and columns 16 j + 4 (s % 4).
-    const int brow = 32 * wave + 8 * (lane >> 4) + ((lane & 15) >> 2);
-    const int bcol_bytes = 8 * (lane & 3);
+    // at row (its group's 8-k block of the wave's k-group slice) + s / 4 and
+    // columns (the wave's column group) + 16 j + 4 (s % 4).
+    const int brow = 32 * kKSteps * (wave / kCGroups) + 8 * (lane >> 4) + ((lane & 15) >> 2);
+    const int bcol_bytes = 8 * (lane & 3) + 32 * NJW * (wave % kCGroups);
 
     auto consume = [&](int d, int s) {
         unsigned char* sa = smem + (s & 1) * T::BUF_BYTES;
@@ -219,19 +231,24 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sa + x_lds[i]) = xr[d][i];
         __syncthreads();
-        as_bf16x8 bf[T::NJ];
 #pragma unroll
-        for (int j = 0; j < T::NJ; ++j) {
-            const unsigned char* p = sa + brow * T::PITCH + 32 * j + bcol_bytes;
-            const as_bf16x4 lo = tr_read(p);
-            const as_bf16x4 hi = tr_read(p + 4 * T::PITCH);
-            bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        for (int kk = 0; kk < kKSteps; ++kk) {
+            as_bf16x8 bf[NJW];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const as_bf16x8 xf = __builtin_bit_cast(as_bf16x8, *reinterpret_cast<const u32x4*>(sa + x_frag[t]));
+            for (int j = 0; j < NJW; ++j) {
+                const unsigned char* p = sa + (brow + 32 * kk) * T::PITCH + 32 * j + bcol_bytes;
+                const as_bf16x4 lo = tr_read(p);
+                const as_bf16x4 hi = tr_read(p + 4 * T::PITCH);
+                bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
 #pragma unroll
-            for (int j = 0; j < T::NJ; ++j) acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bf[j], acc[t][j], 0, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+                const as_bf16x8 xf =
+                    __builtin_bit_cast(as_bf16x8, *reinterpret_cast<const u32x4*>(sa + x_frag[t] + 64 * kk));
+#pragma unroll
+                for (int j = 0; j < NJW; ++j)
+                    acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bf[j], acc[t][j], 0, 0, 0);
+            }
         }
     };
 
@@ -261,16 +278,17 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
     for (int d = 0; d < kDepth; ++d)
         if (s + kDepth + d < ns) consume(d, s + kDepth + d);
 
-    // ---- sum the 8 waves' k-slices in LDS, in wave order ----------------------
+    // ---- sum the k-groups' partial tiles in LDS, in k order -------------------
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < T::NJ; ++j)
+        for (int j = 0; j < NJW; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                red[(wave * kRows + 16 * t + 4 * (lane >> 4) + i) * T::RED_PITCH + 16 * j + (lane & 15)] = acc[t][j][i];
+                red[((wave / kCGroups) * kRows + 16 * t + 4 * (lane >> 4) + i) * T::RED_PITCH +
+                    16 * (NJW * (wave % kCGroups) + j) + (lane & 15)] = acc[t][j][i];
     __syncthreads();
     const int row = tid / (NT / T::OPT);          // 8 threads per row
     const int c0 = (tid % (NT / T::OPT)) * T::OPT;
@@ -278,7 +296,7 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
 #pragma unroll
     for (int c = 0; c < T::OPT; ++c) v[c] = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kKGroups; ++w) {
 #pragma unroll
         for (int c = 0; c < T::OPT; c += 4) {
             const as_f32x4 q = *reinterpret_cast<const as_f32x4*>(&red[(w * kRows + row) * T::RED_PITCH + c0 + c]);
