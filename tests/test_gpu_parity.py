@@ -418,6 +418,19 @@ def test_append_ranks(W, r):
     _append_case(W, inp)
 
 
+@pytest.mark.parametrize("nb,nh,r,E,stages", [(130, 32, 32, 8192, 16), (9, 4, 32, 2560, 5)])
+def test_append_long_slices(W, nb, nh, r, E, stages):
+    """E-slices longer than the four stages a block keeps in flight.  130 x 32
+    heads at r 32 make 96 tiles, so E = 8192 goes into 2 slices of 16 stages:
+    the steady-state loop (each stage requested right after one is consumed),
+    the prologue and the tail, with three 64-row tiles (the last ragged).
+    9 x 4 heads, E = 2560: 2 slices of 5 stages (the tail's refill path)."""
+    ks = E // 256 // stages
+    assert W.append_workspace_bytes(nb, E, nh, r) >= (-(-nh * r // 64)) * 2 * (-(-nb // 64)) * ks * 64 * 64 * 4
+    inp = I.make_ragged_step_inputs(nb, nh, 64, r, E, 2, 16, 16, seed=90 + stages)
+    _append_case(W, inp)
+
+
 def test_append_row_tiles_and_reuse(W):
     """70 sequences (two 64-row tiles, the second ragged), E split into 4
     slices of two stages each; three calls on one workspace.  Equal inputs
