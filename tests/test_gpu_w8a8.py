@@ -127,9 +127,11 @@ def _w8_case(W, nb, E, nh, r, C_dt, seed, L_cap=24):
 
 
 @pytest.mark.parametrize("nb,E,nh,r,C_dt", [
-    (70, 4096, 4, 32, "bf16"),     # two row tiles, E split 8 ways
+    (70, 4096, 4, 32, "bf16"),     # two row tiles, E split 4 ways (two stages per slice)
     (5, 512, 3, 16, "bf16"),       # one stage, ragged column tile
     (9, 1536, 2, 64, "i8"),        # three stages in one slice (no split)
+    (9, 4608, 2, 64, "bf16"),      # nine stages in one slice: four pairs, then one
+    (7, 2560, 4, 32, "i8"),        # five stages in one slice
     (64, 4096, 32, 48, "bf16"),    # the LLaVA-7B-layer step's shape
     (32, 4096, 32, 32, "i8"),      # the int8-cache workload's shape
 ])
