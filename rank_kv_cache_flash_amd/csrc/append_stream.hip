@@ -81,7 +81,7 @@ struct Tile {
     static constexpr int NJ = NT / 16;                       // 16-column groups
     static constexpr int OPT = NT * kRows / 512;             // outputs per thread at the end
     static constexpr int STAGE_BYTES = kStageK * PITCH;
-    static constexpr int XPITCH = kStageK * 2 + 16;          // LDS bytes per x row of a stage
+    static constexpr int XPITCH = kStageK * 2 + 32;          // LDS bytes per x row of a stage (see below)
     static constexpr int XSTAGE_BYTES = kRows * XPITCH;
     static constexpr int BUF_BYTES = STAGE_BYTES + XSTAGE_BYTES;  // one stage of A and x
     static constexpr int RED_PITCH = NT + 4;                 // floats per reduction row (bank spread)
@@ -187,7 +187,9 @@ __global__ __launch_bounds__(512) void append_bf16_kernel(AppendArgs a) {
     // wave-wide load reads two whole 512-byte row pieces (reading the operand
     // layout directly -- 16 rows x 64 bytes per load -- measured 1.2 us slower
     // at the LLaVA-7B step shape).  Rows past nb start past the end of x, where
-    // buffer loads return zeros.  The stage goes to LDS (padded rows) and each
+    // buffer loads return zeros.  The stage goes to LDS (rows padded by 32
+    // bytes: 0.2 us faster than a 16-byte pad at the LLaVA-7B step shape, 48
+    // no better; the pad of A's rows, 16 to 48 bytes, made no difference) and each
     // wave reads back its fragments of 16-row group t: row 16 t + lane % 16,
     // k = the start of the wave's k-group slice (+ 32 per MFMA step),
     // 8 (lane / 16) onwards.
