@@ -23,7 +23,7 @@
 //    beside A (reading the operand layout straight from memory, 16 rows x
 //    64 bytes per load, measured 1.2 us slower at the LLaVA-7B step shape).
 //  * A arrives n-contiguous; its stage is stored to LDS row-major (rows
-//    padded so the reads below are free of bank conflicts) and the B
+//    padded by 32 bytes against bank conflicts) and the B
 //    operands are read with gfx950's transposing LDS read
 //    (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives element
 //    i % 4 of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12,
