@@ -30,11 +30,17 @@ namespace {
 // fixed cost (both factors from L2, q' = B_K q, the projection and, with more
 // than one split, the merge), so splits are only added where they buy
 // parallelism: small batches get enough blocks to cover the CUs, large ones
-// keep whole sequences per block and only cut very long caches (which also
-// evens out ragged lengths).
+// keep whole sequences per block and only cut long caches (which also evens
+// out ragged lengths).
 constexpr long kFillBlocks = 256;       // blocks wanted for a small batch
 constexpr int kMinSplitTokens = 256;    // never cut sequences finer than this
-constexpr int kLongTokens = 2048;       // per-split length cap for large batches
+constexpr int kLongTokens = 2048;       // large batches: caches up to this length stay whole
+// Large batches with longer caches: splits of at most this many tokens
+// (measured on MI355X, 64 sequences x 32 heads, 8192-token cache, ragged
+// lengths: 5 or 6 splits 315.8-316.0 us per step, 4 splits 317.2-317.3, 8
+// splits 317.8-317.9; cutting the 2048-token caches of the 32 x 32-head int8
+// batch into 2 splits instead of 1 cost about 3 us).
+constexpr int kLongSplitTokens = 1536;
 constexpr long kLargeBatchPairs = 1024; // (b, h) pairs that make a batch "large"
 // Split grids at least this large merge in a second launch (measured on
 // MI355X: 8192 blocks gain 5.7 us from it, 160 blocks lose 1.35 us).
@@ -80,7 +86,7 @@ int resolve_splits(int nb, int nh, int L_cap, int n_splits) {
         const long smax = ((long)L_cap + kMinSplitTokens - 1) / kMinSplitTokens;
         if (s > smax) s = smax;
     } else if (bh >= kLargeBatchPairs) {
-        s = ((long)L_cap + kLongTokens - 1) / kLongTokens;
+        if (L_cap > kLongTokens) s = ((long)L_cap + kLongSplitTokens - 1) / kLongSplitTokens;
     }
     if (s < 1) s = 1;
     return (int)s;
