@@ -44,13 +44,14 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fused low-rank decode attn: µs/step and achieved HBM GB/s (% of peak), 1 GPU"
 COLD_BYTES = 1 << 30      # rotate input copies until >= 1 GiB is touched
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ("decode.hip", "decode_bf16_r32.hip", "wsvd_common.hpp", "split_merge.hpp")
+KERNEL_SOURCES = ("decode.hip", "decode_bf16_r32.hip", "wsvd_common.hpp", "split_merge.hpp", "abi.hip")
 
 
 def kernel_src_hash() -> str:
-    """Hash of the split kernel's code: its sources with comments and blank
-    space removed, so that the counter summary stays valid across edits of
-    comments only."""
+    """Hash of the split kernel's code and of the host code that picks its
+    launch shape (the split rule in abi.hip): the sources with comments and
+    blank space removed, so that the counter summary stays valid across
+    edits of comments only."""
     import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
