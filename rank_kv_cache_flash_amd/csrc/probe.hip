@@ -18,16 +18,20 @@ __global__ __launch_bounds__(256) void probe_empty_kernel(float* sink) {
 }
 
 // Block k reads bytes [k * per_block, (k + 1) * per_block) of src; a thread
-// issues all of its (at most kMaxLoads) 16-byte loads before using any.
+// issues all of its (at most kMaxLoads) 16-byte loads before using any.  The
+// loads are buffer loads over the block's share, so a chunk past its end
+// reads zero without a branch: with a guarded load per chunk the compiler
+// waited for the outstanding loads at every guard's join (two loads in
+// flight instead of sixteen), which measured 5.35 against 4.10 us for 5 MB
+// on 160 blocks.
 constexpr int kProbeMaxLoads = 16;
 __global__ __launch_bounds__(256) void probe_stream_kernel(const u32x4* src, size_t chunks_per_block, float* sink) {
-    const u32x4* p = src + blockIdx.x * chunks_per_block;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(src + blockIdx.x * chunks_per_block), 0, (int)(chunks_per_block * 16), 0x00020000);
     u32x4 v[kProbeMaxLoads];
 #pragma unroll
-    for (int i = 0; i < kProbeMaxLoads; ++i) {
-        const size_t c = threadIdx.x + (size_t)256 * i;
-        v[i] = c < chunks_per_block ? load16_stream(p + c) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < kProbeMaxLoads; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (threadIdx.x + 256u * i) * 16u, 0, 2 /* non-temporal */);
     uint32_t x = 0;
 #pragma unroll
     for (int i = 0; i < kProbeMaxLoads; ++i) x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
